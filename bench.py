@@ -1,0 +1,238 @@
+"""Benchmark of one decode step (paged KV write + paged decode attention) on one GPU.
+
+A step is one pass of the whole path over one synthetic batch: write each
+sequence's new K/V row with ``reshape_and_cache``, then ``paged_attention_decode``
+over the updated caches.  Default workload: the Qwen3-0.6B-shaped batch
+(B=32, Hq=16, Hkv=8, D=128, block_size=16, context lengths uniform in
+[128, 2048], bf16 storage, float32 accumulation).
+
+Inputs are resident in HBM before timing starts.  To keep the timed reads
+coming from HBM rather than the 256 MB last-level cache, the step cycles
+through R identical copies of the KV pool (>= 1.25 GiB together).
+
+Prints one JSON line.  ``value`` is the step's algorithmic bytes (KV rows
+read, q read, output written, block-table entries, the write's rows) divided by
+the step time.  ``roofline`` is for the decode kernel alone: algorithmic bytes
+per launch over its mean launch time from HIP events recorded around each
+launch on the stream it runs on.  ``cpu_baseline`` times the float64 CPU oracle
+on a bounded sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "decode-attention KV GB/s and % of HBM peak; µs/step at B=32 Qwen3-0.6B shape"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_reshape_amd", "csrc", "decode.hip")
+
+
+def algorithmic_bytes(inp: dict) -> dict:
+    """Bytes the step must move at least once (no re-reads, no partials)."""
+    w = inp["workload"]
+    ctx = inp["context_lens"].astype(np.int64)
+    elt = w.elt_bytes
+    kv = int(ctx.sum()) * 2 * w.num_kv_heads * w.head_dim * elt
+    qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * elt
+    tables = int(sum(-(-int(c) // w.block_size) for c in ctx)) * 4 + 4 * w.num_seqs
+    n_new = int((inp["slot_mapping"] >= 0).sum())
+    write = 2 * 2 * n_new * w.num_kv_heads * w.head_dim * elt + 8 * w.num_seqs
+    return dict(kv=kv, decode=kv + qo + tables, write=write,
+                step=kv + qo + tables + write)
+
+
+def traffic_record():
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if
+    they were taken on the decode kernel as it is now (source hash matches)."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("decode_hip_sha256") != src:
+        return None
+    return rec
+
+
+def cpu_baseline(inp: dict, budget_s: float) -> dict:
+    """Time the float64 oracle's write + decode on a bounded sample."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    w = inp["workload"]
+    B = w.num_seqs
+    done_bytes = 0
+    seqs_done = 0
+    t0 = time.perf_counter()
+    k, v = oracle.reshape_and_cache(inp["key"], inp["value"], inp["k_cache"],
+                                    inp["v_cache"], inp["slot_mapping"])
+    b = 0
+    while True:
+        sel = [b % B]
+        oracle.decode(inp["q"][sel], k, v, inp["block_tables"][sel],
+                      inp["context_lens"][sel], inp["scale"], w.dtype)
+        c = int(inp["context_lens"][b % B])
+        done_bytes += (c * 2 * w.num_kv_heads * w.head_dim * w.elt_bytes
+                       + 2 * w.num_q_heads * w.head_dim * w.elt_bytes)
+        seqs_done += 1
+        b += 1
+        if time.perf_counter() - t0 >= budget_s and seqs_done >= min(B, 4):
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": (f"float64 numpy oracle: one full-pool KV write, then decode of "
+                       f"{seqs_done} sequences of this batch in order "
+                       f"({dt:.1f} s, {done_bytes / 1e6:.1f} MB of KV rows)")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="qwen3_0p6b", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--partition-size", type=int, default=-1,
+                    help="tokens per partition; -1 = the workload's, 0 = library choice")
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough for 1.25 GiB")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
+              "(no sharding, no collectives); run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import paged_kv_cache_reshape_amd as pa
+    if not os.path.exists(pa.LIB_PATH):
+        from paged_kv_cache_reshape_amd import build as _b
+        _b.build()
+    pa.load_library()
+
+    w = synth.WORKLOADS[args.workload]
+    ps = w.partition_size if args.partition_size < 0 else args.partition_size
+    inp = synth.make_inputs(w)
+    nbytes = algorithmic_bytes(inp)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        if w.dtype == "bf16" and a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    pool_bytes = 2 * inp["k_cache"].nbytes
+    R = args.replicas or max(1, math.ceil(1.25 * 2**30 / pool_bytes))
+    kc0, vc0 = up(inp["k_cache"]), up(inp["v_cache"])
+    kcs = [kc0] + [kc0.clone() for _ in range(R - 1)]
+    vcs = [vc0] + [vc0.clone() for _ in range(R - 1)]
+    q, key, value = up(inp["q"]), up(inp["key"]), up(inp["value"])
+    tables = torch.from_numpy(inp["block_tables"]).to(dev)
+    lens = torch.from_numpy(inp["context_lens"]).to(dev)
+    slots = torch.from_numpy(inp["slot_mapping"]).to(dev)
+    scale = float(inp["scale"])
+    out = torch.empty_like(q)
+    hq, hkv, d, bs = w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    ws_bytes = pa.decode_workspace_bytes(w.num_seqs, hq, hkv, d, tables.shape[1], bs, ps)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    part = pa.decode_partition_size(w.num_seqs, hq, hkv, d, tables.shape[1], bs, ps)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        r = i % R
+        pa.reshape_and_cache(key, value, kcs[r], vcs[r], slots)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.paged_attention_decode(q, kcs[r], vcs[r], tables, lens, scale,
+                                  partition_size=ps, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    k_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    k_mean_s = float(k_ms.mean()) / 1e3
+
+    achieved = nbytes["decode"] / k_mean_s / 1e9
+    traffic = None
+    rec = traffic_record()
+    if rec and rec.get("workload") == w.name and rec.get("partition_size") == part:
+        traffic = rec.get("hbm_bytes_per_launch")
+    res = {
+        "metric": METRIC,
+        "value": round(nbytes["step"] / (ms_step / 1e3) / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{w.name}: B={w.num_seqs} Hq={hq} Hkv={hkv} D={d} "
+                         f"block_size={bs} ctx {w.ctx} {w.dtype}"),
+            "sum_ctx": int(inp["context_lens"].sum()),
+            "partition_size": part,
+            "kv_pool_replicas": R,
+            "step": "reshape_and_cache + paged_attention_decode",
+        },
+        "us_per_step": round(ms_step * 1e3, 3),
+        "tokens_per_s": round(w.num_seqs / (ms_step / 1e3), 1),
+        "decode_us_mean": round(k_mean_s * 1e6, 3),
+        "decode_us_median": round(float(np.median(k_ms)) * 1e3, 3),
+        "decode_kv_gbs": round(nbytes["kv"] / k_mean_s / 1e9, 3),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 3),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "decode_kernel",
+            "bytes_per_launch": nbytes["decode"],
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,192 @@
+/*
+ * libpagedattn -- paged KV-cache write and single-token paged decode attention
+ * for AMD Instinct MI355X (gfx950).  Plain C ABI: raw pointers and sizes only.
+ *
+ * Sources of the operations (web pages this library is written from):
+ *   - barellm README (quanhua92/barellm), paged-cache component list: K/V live
+ *     in fixed-size physical blocks of one [physical_blocks, block_size,
+ *     kv_heads, head_dim] tensor per layer; a per-request block table maps
+ *     logical block pos // block_size to a physical block; the cache owns the
+ *     logical-to-physical writes.  Feature list: token-before-head (NHD)
+ *     layout; one-token batched decode over requests of unequal length; MHA,
+ *     GQA and MQA; paged storage must agree with a contiguous cache.
+ *   - CUDAlab README, "Paged Attention 调用链": one forward entry point for
+ *     paged multi-head attention; Benchmark section: the kv_mul (grouped
+ *     heads) and block_size parameters.
+ *   - LLAISYS README, implemented-features list: C++ backend behind a C API
+ *     called from Python; online softmax with a running max and running sum;
+ *     grouped heads by broadcasting; a multi-block reduction finished by the
+ *     last block to arrive (fence + atomic counter) instead of a second launch.
+ *   - MinivLLM article, "What the Two Benchmark Scripts Compare": paged
+ *     decode attention as its own kernel, blockwise online softmax.
+ *
+ * Conventions for every call:
+ *   - All tensors are dense, row-major, in device memory, 16-byte aligned,
+ *     and owned by the caller.  The library never allocates, frees or
+ *     synchronises; it keeps no state between calls except a per-device
+ *     cache of the compute-unit count.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     runs asynchronously; results are visible after the caller synchronises.
+ *   - Arguments are checked before anything is launched.  On failure the call
+ *     returns a non-zero pa_status, launches nothing, and
+ *     pa_last_error_message() (per host thread) says what was wrong.
+ *   - Tensor *contents* are trusted: a block id outside [0, num_blocks) or a
+ *     context length outside 0 .. max_blocks_per_seq * block_size is never
+ *     dereferenced -- the affected output row is written as NaN instead.
+ *   - Floating-point tensors share one storage type (pa_dtype): float32 or
+ *     bfloat16 (raw 16-bit patterns).  Accumulation is always float32.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, bad combination */
+  PA_ERR_UNSUPPORTED = 2,        /* valid but not built: head_dim, block_size, group */
+  PA_ERR_WORKSPACE_TOO_SMALL = 3,
+  PA_ERR_HIP = 4                 /* the HIP runtime refused a launch or query */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_DTYPE_F32 = 0,
+  PA_DTYPE_BF16 = 1
+} pa_dtype;
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t pa_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* pa_status_string(int32_t status);
+
+/* Detail of the last failed call made by this host thread ("" if none). */
+const char* pa_last_error_message(void);
+
+/*
+ * Paged KV write (the cache's logical-to-physical write; barellm README,
+ * paged-cache component list).
+ *
+ * For each i < num_tokens with s = slot_mapping[i] and 0 <= s < num_blocks *
+ * block_size: copies key[i, :, :] to k_cache[s / block_size, s % block_size,
+ * :, :] and value[i, :, :] to v_cache[...] -- an exact copy of the stored
+ * bits.  Rows with s < 0 are skipped (padding); rows with s past the pool are
+ * skipped too.  Slots that appear twice in one call are written in no
+ * particular order.
+ *
+ *   key, value      [num_tokens, num_kv_heads, head_dim]      (read)
+ *   k_cache, v_cache[num_blocks, block_size, num_kv_heads, head_dim] (written)
+ *   slot_mapping    [num_tokens] int64                        (read)
+ *
+ * num_tokens == 0 is a valid no-op.  head_dim in {64, 128}; block_size in
+ * {16, 32}.
+ */
+pa_status pa_reshape_and_cache(const void* key, const void* value,
+                               void* k_cache, void* v_cache,
+                               const int64_t* slot_mapping,
+                               int32_t num_tokens, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t num_blocks,
+                               int32_t block_size, pa_dtype dtype,
+                               void* stream);
+
+/*
+ * The partition size (tokens) pa_paged_attention_decode will use for these
+ * sizes: `requested` itself if it is a positive multiple of block_size no
+ * larger than 64 * block_size, the library's own choice if `requested` is 0,
+ * or -1 if `requested` is invalid.
+ */
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int32_t block_size,
+                                 int32_t requested);
+
+/*
+ * Bytes of workspace pa_paged_attention_decode needs for these sizes (the
+ * split-K partial results and one counter per (sequence, KV head)); 0 on
+ * invalid sizes.  The workspace must be zero-filled once after allocation;
+ * each call leaves its counters at zero again, so it can be reused by later
+ * calls on the same stream without clearing.  Two calls that may run at the
+ * same time must not share a workspace.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int32_t block_size,
+                                 int32_t partition_size);
+
+/*
+ * Single-token decode attention over a paged KV cache (barellm README,
+ * feature list: one-token batched decode with unequal lengths; paged-cache
+ * list: position -> block table -> physical block).
+ *
+ * For each sequence b < num_seqs with L = context_lens[b] (the cached tokens,
+ * including the one written this step) and each query head h < num_q_heads,
+ * with g = h / (num_q_heads / num_kv_heads):
+ *     row t < L is  k_cache[block_tables[b, t / block_size], t % block_size, g, :]
+ *     s_t        =  scale * dot(q[b, h, :], k_t)
+ *     out[b,h,:] =  sum_t exp(s_t - max s) v_t / sum_t exp(s_t - max s)
+ * in float32 arithmetic, rounded once to the storage type (round to nearest
+ * even).  L == 0 writes a zero row.  Table entries at or past
+ * ceil(L / block_size) are never read.
+ *
+ * Sequences longer than one partition are split into partitions of
+ * `partition_size` tokens (0 = library choice, see
+ * pa_decode_partition_size); each partition's softmax state (max, sum,
+ * unnormalised output) goes to the workspace and the last partition to finish
+ * merges them with a log-sum-exp reduction in the same launch.  Results do
+ * not depend on the order in which partitions finish (bit-identical reruns).
+ *
+ *   out            [num_seqs, num_q_heads, head_dim]                   (written)
+ *   q              [num_seqs, num_q_heads, head_dim]                   (read)
+ *   k_cache, v_cache [num_blocks, block_size, num_kv_heads, head_dim]  (read)
+ *   block_tables   [num_seqs, max_blocks_per_seq] int32                (read)
+ *   context_lens   [num_seqs] int32                                    (read)
+ *   workspace      >= pa_decode_workspace_bytes(...) bytes, zeroed once
+ *                  (may be NULL if that size is 0)
+ *
+ * head_dim in {64, 128}; block_size in {16, 32}; num_q_heads a multiple of
+ * num_kv_heads with a group of 1, 2, 4, 8, 16 or 32 query heads per KV head.
+ */
+pa_status pa_paged_attention_decode(void* out, const void* q,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables,
+                                    const int32_t* context_lens,
+                                    int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t num_blocks, int32_t block_size,
+                                    int32_t max_blocks_per_seq, float scale,
+                                    int32_t partition_size,
+                                    void* workspace, size_t workspace_bytes,
+                                    pa_dtype dtype, void* stream);
+
+/*
+ * Test and debugging aid: the exact gather a dense-attention engine would do
+ * (barellm README, feature list: pages gathered into dense tensors).
+ *
+ * k_dense[b, t] = k_cache[block_tables[b, t / block_size], t % block_size]
+ * for t < context_lens[b], all-zero bytes for t >= context_lens[b]; the same
+ * for V.  Rows whose block id is outside [0, num_blocks) are filled with 0xFF
+ * bytes (NaN in both storage types).
+ *
+ *   k_dense, v_dense [num_seqs, max_blocks_per_seq * block_size,
+ *                     num_kv_heads, head_dim]                          (written)
+ */
+pa_status pa_debug_gather_kv(void* k_dense, void* v_dense,
+                             const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables,
+                             const int32_t* context_lens,
+                             int32_t num_seqs, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t num_blocks,
+                             int32_t block_size, int32_t max_blocks_per_seq,
+                             pa_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,154 @@
+"""The C-ABI library: it loads, exports every declared symbol, and its host-side
+checks and size rules behave as documented.  No GPU: only calls that return
+before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_reshape_amd as pa
+from paged_kv_cache_reshape_amd import build as pabuild
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "pagedattn.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.LIB_PATH):
+        pabuild.build()
+    return pa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("pa_reshape_and_cache", "pa_paged_attention_decode",
+              "pa_decode_workspace_bytes", "pa_decode_partition_size",
+              "pa_debug_gather_kv", "pa_status_string", "pa_last_error_message",
+              "pa_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.pa_status_string(0) == b"ok"
+    assert lib.pa_status_string(3) == b"workspace too small"
+    assert lib.pa_status_string(99) == b"unknown status"
+    assert lib.pa_version() >= 100
+
+
+def _decode(lib, **kw):
+    a = dict(out=16, q=16, k=16, v=16, bt=16, cl=16, B=4, Hq=4, Hkv=2, D=64, nb=32,
+             bs=16, mb=4, scale=0.125, ps=0, ws=None, wsb=0, dt=0)
+    a.update(kw)
+    return lib.pa_paged_attention_decode(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["B"], a["Hq"], a["Hkv"],
+        a["D"], a["nb"], a["bs"], a["mb"], a["scale"], a["ps"], a["ws"], a["wsb"],
+        a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=5), INVALID),
+    (dict(Hq=6, Hkv=4), INVALID),
+    (dict(Hq=12, Hkv=4), UNSUPPORTED),      # group of 3
+    (dict(D=96), UNSUPPORTED),
+    (dict(bs=8), UNSUPPORTED),
+    (dict(ps=24), INVALID),                 # not a multiple of block_size
+    (dict(ps=16 * 65), INVALID),            # more than 64 blocks
+    (dict(Hkv=0), INVALID),
+    (dict(nb=0), INVALID),
+    (dict(B=-1), INVALID),
+    (dict(q=None), INVALID),
+    (dict(k=8), INVALID),                   # misaligned
+    (dict(mb=400, ps=16), WS_SMALL),        # needs partials, none given
+    (dict(B=0, q=None, out=None), OK),      # empty batch: nothing to do
+])
+def test_decode_argument_checks(lib, kw, status):
+    assert _decode(lib, **kw) == status
+    if status:
+        assert lib.pa_last_error_message() != b""
+
+
+def test_write_argument_checks(lib):
+    f = lib.pa_reshape_and_cache
+    assert f(16, 16, 16, 16, 16, 0, 2, 64, 32, 16, 0, None) == OK  # no tokens
+    assert f(16, 16, 16, 16, 16, -1, 2, 64, 32, 16, 0, None) == INVALID
+    assert f(None, 16, 16, 16, 16, 4, 2, 64, 32, 16, 0, None) == INVALID
+    assert f(16, 16, 16, 16, 16, 4, 2, 48, 32, 16, 0, None) == UNSUPPORTED
+    assert f(16, 16, 16, 16, 16, 4, 2, 64, 32, 64, 0, None) == UNSUPPORTED
+    assert f(16, 16, 16, 16, 16, 4, 2, 64, 32, 16, 9, None) == INVALID
+    assert f(16, 24, 16, 16, 16, 4, 2, 64, 32, 16, 0, None) == INVALID  # misaligned
+
+
+def test_gather_argument_checks(lib):
+    f = lib.pa_debug_gather_kv
+    assert f(16, 16, 16, 16, 16, 16, 0, 2, 64, 32, 16, 4, 0, None) == OK
+    assert f(16, 16, 16, 16, 16, 16, 4, 2, 64, 32, 16, 0, 0, None) == INVALID
+    assert f(None, 16, 16, 16, 16, 16, 4, 2, 64, 32, 16, 4, 0, None) == INVALID
+
+
+def test_partition_size_rule(lib):
+    # explicit sizes are honoured when valid
+    assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 512) == 512
+    assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 500) == -1
+    assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 64) == 1024
+    assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 65) == -1
+    # the library's choice is a multiple of the block size, 4..64 blocks
+    for args in [(32, 16, 8, 128, 128, 16), (64, 32, 8, 64, 256, 16),
+                 (256, 32, 32, 128, 32, 32), (4, 4, 2, 64, 4, 16)]:
+        p = pa.decode_partition_size(*args, 0)
+        assert p % args[-1] == 0 and 4 <= p // args[-1] <= 64
+
+
+def test_workspace_size_rule(lib):
+    # no workspace when every sequence fits one partition
+    assert pa.decode_workspace_bytes(4, 4, 2, 64, 4, 16, 64) == 0
+    # otherwise: G*D floats of output + 2 floats per (seq, kv head, partition,
+    # head), plus one int32 counter per (seq, kv head), each 256-byte aligned
+    B, Hq, Hkv, D, mb, bs, ps = 8, 32, 8, 128, 2048, 16, 512
+    parts = mb * bs // ps
+    rows = B * Hkv * parts * (Hq // Hkv)
+
+    def al(x):
+        return (x + 255) // 256 * 256
+    want = al(rows * D * 4) + al(rows * 2 * 4) + al(B * Hkv * 4)
+    assert pa.decode_workspace_bytes(B, Hq, Hkv, D, mb, bs, ps) == want
+    assert pa.decode_workspace_bytes(B, Hq, Hkv, D, mb, bs, 24) == 0  # invalid
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 2, 64)
+    with pytest.raises(ValueError):
+        pa.paged_attention_decode(q, torch.zeros(1, 16, 1, 64), torch.zeros(1, 16, 1, 64),
+                                  torch.zeros(1, 1, dtype=torch.int32),
+                                  torch.ones(1, dtype=torch.int32), 0.1)
+
+
+def test_one_hip_runtime_in_process(lib):
+    """The library binds to the HIP runtime PyTorch already loaded: the process
+    maps exactly one libamdhip64, PyTorch's own copy."""
+    maps = open("/proc/self/maps").read()
+    hips = sorted(set(re.findall(r"\S*libamdhip64\S*", maps)))
+    assert len(hips) == 1, hips
+    assert hips[0].startswith(pabuild.torch_lib_dir()), hips
+
+
+def test_ctypes_signatures_match_header(lib):
+    assert lib.pa_decode_workspace_bytes.restype is ctypes.c_size_t
+    assert len(lib.pa_paged_attention_decode.argtypes) == 19
+    assert len(lib.pa_reshape_and_cache.argtypes) == 12
+    assert len(lib.pa_debug_gather_kv.argtypes) == 14

@@ -1,0 +1,322 @@
+"""The HIP path against the float64 oracle on the GPU, through the C ABI.
+
+Bit-exact: the KV write, the dense gather (block-table indexing), the
+single-token and hard-max closed forms, block relabelling, NaN poisoning,
+reruns.  Within tolerance (bf16: 2e-3 + 1e-2|y|; f32: 1e-5 + 1e-5|y|): every
+decode output against the oracle.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import paged_kv_cache_reshape_amd as pa
+from tests import _gpu as G
+from tests import _pins as P
+
+pytestmark = pytest.mark.gpu
+
+ALL = ["tiny_f32", "qwen3_0p6b", "llama32_1b", "long_splitk", "mha_large", "mqa_large"]
+# Small shapes that still span several blocks, partitions and a ragged tail.
+EXTRA = {
+    "f32_d128_bs32_g4": synth.Workload("f32_d128_bs32_g4", 5, 16, 4, 128, 32, "f32",
+                                       ("uniform", 1, 700), num_blocks=160, seed=31),
+    "bf16_d64_bs32_g8": synth.Workload("bf16_d64_bs32_g8", 7, 16, 2, 64, 32, "bf16",
+                                       ("uniform", 1, 900), num_blocks=260, seed=32),
+    "bf16_d128_bs16_g16": synth.Workload("bf16_d128_bs16_g16", 6, 32, 2, 128, 16,
+                                         "bf16", ("uniform", 1, 1500), seed=33),
+    "f32_d64_bs16_g1": synth.Workload("f32_d64_bs16_g1", 9, 4, 4, 64, 16, "f32",
+                                      ("uniform", 1, 300), seed=34),
+    "bf16_d64_bs16_g2": synth.Workload("bf16_d64_bs16_g2", 11, 8, 4, 64, 16, "bf16",
+                                       ("uniform", 1, 2000), seed=35),
+}
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def inputs_for(name, **kw):
+    if name in EXTRA:
+        return synth.make_inputs(EXTRA[name], **kw)
+    if not kw:
+        return G.cached_inputs(name)
+    return synth.make_inputs(synth.WORKLOADS[name], **kw)
+
+
+def gpu_step(d, partition_size=0, write=True):
+    """One step on the GPU: the KV write, then decode.  Returns out (device)."""
+    if write:
+        pa.reshape_and_cache(d["key"], d["value"], d["k_cache"], d["v_cache"],
+                             d["slot_mapping"])
+    return pa.paged_attention_decode(d["q"], d["k_cache"], d["v_cache"],
+                                     d["block_tables"], d["context_lens"], d["scale"],
+                                     partition_size=partition_size)
+
+
+def oracle_step(inp, seqs=None):
+    """The oracle's write + decode, optionally on a subset of sequences."""
+    w = inp["workload"]
+    k, v = oracle.reshape_and_cache(inp["key"], inp["value"], inp["k_cache"],
+                                    inp["v_cache"], inp["slot_mapping"])
+    sel = slice(None) if seqs is None else np.asarray(seqs)
+    out = oracle.decode(inp["q"][sel], k, v, inp["block_tables"][sel],
+                        inp["context_lens"][sel], inp["scale"], w.dtype)
+    return out, (k, v)
+
+
+# ------------------------------------------------------------------ KV write
+@pytest.mark.parametrize("name", ALL)
+def test_write_bit_exact(name):
+    inp = inputs_for(name)
+    w = inp["workload"]
+    say("reshape_and_cache", name, w)
+    d = G.upload(inp)
+    slots = inp["slot_mapping"].copy()
+    slots[0] = -1                                 # padding row: skipped
+    if len(slots) > 2:
+        slots[1] = inp["num_blocks"] * w.block_size  # past the pool: skipped
+    d["slot_mapping"] = torch.from_numpy(slots).cuda()
+    pa.reshape_and_cache(d["key"], d["value"], d["k_cache"], d["v_cache"],
+                         d["slot_mapping"])
+    torch.cuda.synchronize()
+    oslots = slots.copy()
+    oslots[oslots >= inp["num_blocks"] * w.block_size] = -1
+    k_ref, v_ref = oracle.reshape_and_cache(inp["key"], inp["value"], inp["k_cache"],
+                                            inp["v_cache"], oslots)
+    assert np.array_equal(G.host_storage(d["k_cache"]), k_ref)
+    assert np.array_equal(G.host_storage(d["v_cache"]), v_ref)
+
+
+@pytest.mark.parametrize("dtype,hkv,d", [("bf16", 8, 128), ("f32", 2, 64),
+                                         ("bf16", 1, 64)])
+def test_write_many_tokens(dtype, hkv, d):
+    """A prefill-sized write (N >> B): 3000 distinct slots in a 400-block pool."""
+    rng = np.random.default_rng(77)
+    nb, bs, n = 400, 16, 3000
+    say("reshape_and_cache many", dtype, hkv, d)
+    shape = (nb, bs, hkv, d)
+    kc = synth._draw(rng, shape, 1.0, dtype)
+    vc = synth._draw(rng, shape, 1.0, dtype)
+    key = synth._draw(rng, (n, hkv, d), 1.0, dtype)
+    val = synth._draw(rng, (n, hkv, d), 1.0, dtype)
+    slots = rng.permutation(nb * bs)[:n].astype(np.int64)
+    slots[::97] = -1
+    dk, dv = G.dev_tensor(kc, dtype), G.dev_tensor(vc, dtype)
+    pa.reshape_and_cache(G.dev_tensor(key, dtype), G.dev_tensor(val, dtype), dk, dv,
+                         torch.from_numpy(slots).cuda())
+    k_ref, v_ref = oracle.reshape_and_cache(key, val, kc, vc, slots)
+    assert np.array_equal(G.host_storage(dk), k_ref)
+    assert np.array_equal(G.host_storage(dv), v_ref)
+
+
+# ------------------------------------------------------------------ gather
+@pytest.mark.parametrize("name", ALL + list(EXTRA))
+def test_gather_bit_exact(name):
+    inp = inputs_for(name)
+    say("debug_gather_kv", name)
+    d = G.upload(inp)
+    nseq = 24 if name in ("mha_large", "mqa_large") else None
+    bt, cl = d["block_tables"], d["context_lens"]
+    if nseq:
+        bt, cl = bt[:nseq].contiguous(), cl[:nseq].contiguous()
+    kd, vd = pa.debug_gather_kv(d["k_cache"], d["v_cache"], bt, cl)
+    tables = inp["block_tables"][:nseq] if nseq else inp["block_tables"]
+    lens = inp["context_lens"][:nseq] if nseq else inp["context_lens"]
+    assert np.array_equal(G.host_storage(kd), oracle.gather_kv(inp["k_cache"], tables, lens))
+    assert np.array_equal(G.host_storage(vd), oracle.gather_kv(inp["v_cache"], tables, lens))
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("name", ["tiny_f32", "qwen3_0p6b", "llama32_1b", "mha_large",
+                                  "mqa_large"] + list(EXTRA))
+def test_decode_matches_oracle(name):
+    inp = inputs_for(name)
+    w = inp["workload"]
+    say("write+decode", name, "partition", w.partition_size)
+    d = G.upload(inp)
+    out = G.host_f64(gpu_step(d, w.partition_size))
+    ref, (k_ref, v_ref) = oracle_step(inp)
+    assert np.array_equal(G.host_storage(d["k_cache"]), k_ref)
+    G.assert_close(out, ref, w.dtype, name)
+
+
+def test_decode_long_split_k_sampled():
+    """32,768-token sequences, 512-token partitions (64 per sequence), merged
+    in the same launch; the oracle checks every head of three sequences."""
+    inp = inputs_for("long_splitk")
+    w = inp["workload"]
+    say("write+decode long_splitk partition", w.partition_size)
+    d = G.upload(inp)
+    out = G.host_f64(gpu_step(d, w.partition_size))
+    seqs = [0, 3, 7]
+    ref, _ = oracle_step(inp, seqs)
+    G.assert_close(out[seqs], ref, w.dtype, "long_splitk")
+
+
+@pytest.mark.parametrize("ps", [16, 64, 256, 1024])
+def test_partition_sizes_agree(ps):
+    inp = inputs_for("qwen3_0p6b")
+    say("decode qwen3 partition", ps)
+    d = G.upload(inp)
+    out = G.host_f64(gpu_step(d, ps))
+    ref, _ = oracle_step(inp)
+    G.assert_close(out, ref, "bf16", f"partition {ps}")
+
+
+def test_max_context_everywhere():
+    """Every sequence fills its whole table (2048 tokens = 128 blocks)."""
+    w = synth.WORKLOADS["qwen3_0p6b"]
+    inp = synth.make_inputs(w, context_lens=np.full(w.num_seqs, 2048, np.int32))
+    say("decode qwen3 ctx=2048 all")
+    d = G.upload(inp)
+    out = G.host_f64(gpu_step(d))
+    seqs = [0, 13, 31]
+    ref, _ = oracle_step(inp, seqs)
+    G.assert_close(out[seqs], ref, "bf16", "max ctx")
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "qwen3_0p6b", "bf16_d64_bs32_g8",
+                                  "f32_d128_bs32_g4", "mqa_large"])
+def test_single_token_exact(name):
+    """P3 on the GPU: one cached token -> out is exactly that V row."""
+    w = EXTRA.get(name) or synth.WORKLOADS[name]
+    inp = synth.make_inputs(w, context_lens=np.ones(w.num_seqs, dtype=np.int32))
+    say("decode ctx=1", name)
+    d = G.upload(inp)
+    out = G.host_storage(gpu_step(d))
+    _, (k_ref, v_ref) = oracle_step(inp)
+    grp = w.num_q_heads // w.num_kv_heads
+    for b in range(w.num_seqs):
+        vrow = v_ref[int(inp["block_tables"][b, 0]), 0]
+        expect = np.repeat(vrow, grp, axis=0)  # head h reads kv head h // grp
+        assert np.array_equal(out[b], expect), b
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "gqa4_bf16"])
+def test_onehot_exact(name):
+    """P4 on the GPU: scale 1e5 -> out is exactly V of the top-scoring row."""
+    w = (synth.WORKLOADS["tiny_f32"] if name == "tiny_f32" else
+         synth.Workload("gqa4_bf16", 6, 8, 2, 32 * 2, 16, "bf16", ("uniform", 1, 100),
+                        num_blocks=48, seed=21))
+    inp, (k, v), best = P.onehot_inputs(w)
+    say("decode one-hot", name)
+    d = G.upload(inp)
+    d["k_cache"] = G.dev_tensor(k, w.dtype)
+    d["v_cache"] = G.dev_tensor(v, w.dtype)
+    d["scale"] = 1e5
+    out = G.host_f64(gpu_step(d, write=False))
+    for (b, h), row in best.items():
+        assert np.array_equal(out[b, h], row), (b, h)
+
+
+def test_block_relabelling_bit_identical():
+    """P5 on the GPU: permuting physical ids (table updated) changes no bit."""
+    inp = inputs_for("qwen3_0p6b")
+    say("decode qwen3 relabelled")
+    d = G.upload(inp)
+    base = G.host_storage(gpu_step(d))
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(inp["num_blocks"])
+    k, v = G.host_storage(d["k_cache"]), G.host_storage(d["v_cache"])
+    k2, v2 = np.empty_like(k), np.empty_like(v)
+    k2[perm], v2[perm] = k, v
+    t = inp["block_tables"]
+    t2 = np.where(t >= 0, perm[np.clip(t, 0, None)], t).astype(np.int32)
+    d2 = dict(d, k_cache=G.dev_tensor(k2, "bf16"), v_cache=G.dev_tensor(v2, "bf16"),
+              block_tables=torch.from_numpy(t2).cuda())
+    assert np.array_equal(G.host_storage(gpu_step(d2, write=False)), base)
+
+
+def test_mqa_equals_replicated_mha():
+    """P6 on the GPU: the MQA batch equals MHA over the KV head copied 32x."""
+    inp = inputs_for("mqa_large")
+    say("decode mqa vs replicated mha")
+    d = G.upload(inp)
+    mqa = G.host_f64(gpu_step(d))
+    k = d["k_cache"].repeat_interleave(32, dim=2).contiguous()
+    v = d["v_cache"].repeat_interleave(32, dim=2).contiguous()
+    mha = G.host_f64(pa.paged_attention_decode(d["q"], k, v, d["block_tables"],
+                                               d["context_lens"], d["scale"]))
+    ref, _ = oracle_step(inp)
+    G.assert_close(mqa, ref, "bf16", "mqa")
+    G.assert_close(mha, ref, "bf16", "replicated mha")
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "qwen3_0p6b", "bf16_d64_bs32_g8"])
+def test_nan_poison_bit_identical(name):
+    """P13 on the GPU: NaN in unread slots and poison-padded tables change no bit."""
+    w = EXTRA.get(name) or synth.WORKLOADS[name]
+    clean = synth.make_inputs(w)
+    dirty = synth.make_inputs(w, poison=True)
+    say("decode poison", name)
+    a = G.host_storage(gpu_step(G.upload(clean)))
+    b = G.host_storage(gpu_step(G.upload(dirty)))
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("name,ps", [("qwen3_0p6b", 64), ("long_splitk", 512)])
+def test_rerun_bit_identical(name, ps):
+    """P14: partitions finish in any order, the merge does not depend on it."""
+    inp = inputs_for(name)
+    say("decode rerun", name, ps)
+    d = G.upload(inp)
+    a = G.host_storage(gpu_step(d, ps))
+    for _ in range(3):
+        b = G.host_storage(gpu_step(d, ps, write=False))
+        assert np.array_equal(a, b)
+
+
+def test_empty_sequences_give_zero_rows():
+    w = synth.WORKLOADS["qwen3_0p6b"]
+    ctx = G.cached_inputs("qwen3_0p6b")["context_lens"].copy()
+    ctx[[0, 5, 31]] = 0
+    inp = synth.make_inputs(w, context_lens=ctx)
+    say("decode with empty sequences")
+    d = G.upload(inp)
+    out = G.host_f64(gpu_step(d, 64))
+    assert np.all(out[[0, 5, 31]] == 0)
+    ref, _ = oracle_step(inp)
+    G.assert_close(out, ref, "bf16", "empty rows")
+
+
+def test_bad_table_entries_give_nan_rows_only():
+    """A block id outside the pool, or a length past the table, is never
+    dereferenced: that sequence's rows become NaN, the others are unchanged."""
+    inp = inputs_for("qwen3_0p6b")
+    say("decode bad table entries")
+    d = G.upload(inp)
+    base = G.host_storage(gpu_step(d, 256))
+    t = inp["block_tables"].copy()
+    ctx = inp["context_lens"].copy()
+    t[2, 0] = inp["num_blocks"]        # one past the pool
+    t[4, (ctx[4] - 1) // 16] = -5      # negative, in the last used block
+    ctx[6] = 129 * 16                  # longer than the table
+    d2 = dict(d, block_tables=torch.from_numpy(t).cuda(),
+              context_lens=torch.from_numpy(ctx).cuda())
+    out = gpu_step(d2, 256, write=False)
+    got = G.host_f64(out)
+    bad = [2, 4, 6]
+    assert np.all(np.isnan(got[bad]))
+    keep = [b for b in range(32) if b not in bad]
+    assert np.array_equal(G.host_storage(out)[keep], base[keep])
+
+
+def test_side_stream_and_given_out():
+    """Work goes on the caller's current stream; `out` may be supplied."""
+    inp = inputs_for("qwen3_0p6b")
+    say("decode on side stream")
+    d = G.upload(inp)
+    base = G.host_storage(gpu_step(d))
+    s = torch.cuda.Stream()
+    out = torch.full_like(d["q"], float("nan"))
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        pa.paged_attention_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                  d["context_lens"], d["scale"], out=out)
+    s.synchronize()
+    assert np.array_equal(G.host_storage(out), base)
