@@ -153,7 +153,8 @@ def main() -> int:
     out = torch.empty_like(q)
     hq, hkv, d, bs = w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
     ws_bytes = pa.decode_workspace_bytes(w.num_seqs, hq, hkv, d, tables.shape[1], bs, ps)
-    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    counters = torch.zeros(w.num_seqs * hkv, dtype=torch.int32, device=dev)
     part = pa.decode_partition_size(w.num_seqs, hq, hkv, d, tables.shape[1], bs, ps)
 
     stream = torch.cuda.current_stream(dev)
@@ -164,7 +165,8 @@ def main() -> int:
         if ev is not None:
             ev[0].record(stream)
         pa.paged_attention_decode(q, kcs[r], vcs[r], tables, lens, scale,
-                                  partition_size=ps, out=out, workspace=ws)
+                                  partition_size=ps, out=out, workspace=ws,
+                                  counters=counters)
         if ev is not None:
             ev[1].record(stream)
 

@@ -107,12 +107,12 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
                                  int32_t requested);
 
 /*
- * Bytes of workspace pa_paged_attention_decode needs for these sizes (the
- * split-K partial results and one counter per (sequence, KV head)); 0 on
- * invalid sizes.  The workspace must be zero-filled once after allocation;
- * each call leaves its counters at zero again, so it can be reused by later
- * calls on the same stream without clearing.  Two calls that may run at the
- * same time must not share a workspace.
+ * Bytes of workspace pa_paged_attention_decode needs for these sizes: the
+ * split-K partial results (per sequence, KV head, partition and query head:
+ * head_dim floats of unnormalised output plus the running max and sum).
+ * 0 when no sequence can span more than one partition, and 0 on invalid
+ * sizes.  The workspace needs no initialisation.  Two calls that may run at
+ * the same time must not share a workspace.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim,
@@ -137,7 +137,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * Sequences longer than one partition are split into partitions of
  * `partition_size` tokens (0 = library choice, see
  * pa_decode_partition_size); each partition's softmax state (max, sum,
- * unnormalised output) goes to the workspace and the last partition to finish
+ * unnormalised output) goes to the workspace and the last partition of that
+ * (sequence, KV head) to finish -- found with an atomic arrival counter --
  * merges them with a log-sum-exp reduction in the same launch.  Results do
  * not depend on the order in which partitions finish (bit-identical reruns).
  *
@@ -146,8 +147,13 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *   k_cache, v_cache [num_blocks, block_size, num_kv_heads, head_dim]  (read)
  *   block_tables   [num_seqs, max_blocks_per_seq] int32                (read)
  *   context_lens   [num_seqs] int32                                    (read)
- *   workspace      >= pa_decode_workspace_bytes(...) bytes, zeroed once
- *                  (may be NULL if that size is 0)
+ *   workspace      >= pa_decode_workspace_bytes(...) bytes, 256-byte
+ *                  aligned, contents ignored (NULL allowed if that size is 0)
+ *   counters       >= num_seqs * num_kv_heads int32 arrival counters; all
+ *                  zero before the first call; every call leaves the
+ *                  counters it used at zero again, so one counter array can
+ *                  serve any later call (any sizes) on the same stream
+ *                  (NULL allowed if the workspace size is 0)
  *
  * head_dim in {64, 128}; block_size in {16, 32}; num_q_heads a multiple of
  * num_kv_heads with a group of 1, 2, 4, 8, 16 or 32 query heads per KV head.
@@ -162,6 +168,7 @@ pa_status pa_paged_attention_decode(void* out, const void* q,
                                     int32_t max_blocks_per_seq, float scale,
                                     int32_t partition_size,
                                     void* workspace, size_t workspace_bytes,
+                                    int32_t* counters, int64_t num_counters,
                                     pa_dtype dtype, void* stream);
 
 /*

@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "LIB_PATH", "load_library", "PagedAttnError", "reshape_and_cache",
     "paged_attention_decode", "decode_partition_size", "decode_workspace_bytes",
-    "debug_gather_kv", "workspace_for",
+    "debug_gather_kv", "workspace_for", "counters_for",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
@@ -74,11 +74,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.pa_paged_attention_decode.restype = i32
         lib.pa_paged_attention_decode.argtypes = [
             vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
-            vp, sz, i32, vp]
+            vp, sz, vp, i64, i32, vp]
         lib.pa_debug_gather_kv.restype = i32
         lib.pa_debug_gather_kv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                            i32, i32, i32, vp]
-        _ = i64
         _lib = lib
         return lib
 
@@ -152,30 +151,49 @@ def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
 
 
 _workspaces: dict = {}
+_counters: dict = {}
 
 
 def workspace_for(device: torch.device, nbytes: int) -> torch.Tensor | None:
-    """A zero-filled workspace of >= nbytes for this device and current stream.
+    """A workspace of >= nbytes for this device and current stream (cached).
 
-    Cached per (device, stream): the decode kernel leaves its counters at zero,
-    so the buffer is only cleared when it is first allocated.
+    Its contents need no initialisation; it is reused by later calls on the
+    same stream and replaced by a larger one when needed.
     """
     if nbytes == 0:
         return None
     key = (device.index, _stream(device))
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
+
+
+def counters_for(device: torch.device, count: int) -> torch.Tensor:
+    """Zero-initialised int32 arrival counters (>= count) for this device and
+    current stream.  Every decode call leaves the counters it used at zero, so
+    one array serves all later calls on the stream, whatever their sizes."""
+    key = (device.index, _stream(device))
+    c = _counters.get(key)
+    if c is None or c.numel() < count:
+        c = torch.zeros(max(count, 1024), dtype=torch.int32, device=device)
+        _counters[key] = c
+    return c
 
 
 def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            block_tables: torch.Tensor, context_lens: torch.Tensor,
                            scale: float, partition_size: int = 0,
                            out: torch.Tensor | None = None,
-                           workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Decode attention ``out[B, Hq, D]`` over the paged caches."""
+                           workspace: torch.Tensor | None = None,
+                           counters: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention ``out[B, Hq, D]`` over the paged caches.
+
+    ``workspace`` (uint8, contents ignored) and ``counters`` (int32, all zero
+    before first use, kept zero by every call) default to per-stream buffers
+    managed here.
+    """
     lib = load_library()
     dev = _same_device(q, k_cache, v_cache, block_tables, context_lens)
     _need(q.dim() == 3, "q must be [B, Hq, D]")
@@ -201,11 +219,19 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         workspace = workspace_for(dev, need)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if need and counters is None:
+        counters = counters_for(dev, B * hkv)
+    if counters is not None:
+        _need(counters.dtype == torch.int32 and counters.device == dev
+              and counters.is_contiguous(), "counters must be contiguous int32 on the GPU")
+    c_ptr = counters.data_ptr() if counters is not None else None
+    c_len = counters.numel() if counters is not None else 0
     with torch.cuda.device(dev):
         st = lib.pa_paged_attention_decode(
             out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             block_tables.data_ptr(), context_lens.data_ptr(), B, hq, hkv, d, nb, bs,
-            max_blocks, float(scale), partition_size, ws_ptr, ws_len, dt, _stream(dev))
+            max_blocks, float(scale), partition_size, ws_ptr, ws_len, c_ptr, c_len, dt,
+            _stream(dev))
     _check(st, "pa_paged_attention_decode")
     return out
 

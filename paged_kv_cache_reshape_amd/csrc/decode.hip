@@ -20,10 +20,16 @@
 //     waves through LDS at the end;
 //   * a sequence with more than one partition writes each partition's state
 //     to the workspace; the last workgroup of that (sequence, kv head) to
-//     arrive (atomic counter after a device-scope release fence) merges them
-//     with a log-sum-exp reduction and writes the output, so there is no
-//     second launch (the last-block pattern of the LLAISYS README, CUDA
-//     argmax item).
+//     arrive (atomic arrival counter) merges them with a log-sum-exp
+//     reduction and writes the output, so there is no second launch (the
+//     last-block pattern of the LLAISYS README, CUDA argmax item).
+//   * MI355X has one L2 per XCD and the L2s are not coherent with each other;
+//     a device-scope fence therefore writes back and invalidates the whole L2
+//     of the XCD, which costs far more than the data it protects.  Partition
+//     states are instead stored and loaded with system-scope atomic accesses
+//     (they bypass the non-coherent L2s), each workgroup waits for its own
+//     stores to complete before it counts itself in, and the merger loads
+//     only after it has seen every arrival: no cache-wide maintenance.
 #include "common.hpp"
 
 #include <math.h>
@@ -39,7 +45,7 @@ struct DecodeArgs {
   const int32_t* context_lens;
   float* ws_acc;      // [B, Hkv, max_parts, G, D]  unnormalised partition outputs
   float* ws_ml;       // [B, Hkv, max_parts, G, 2]  (max, sum) per partition, log2 units
-  int32_t* ws_count;  // [B, Hkv]                   arrivals, reset by the merger
+  int32_t* counters;  // [B, Hkv]                   arrivals, reset by the merger
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t num_blocks;
@@ -104,6 +110,15 @@ __device__ __forceinline__ void store_out(F32, void* base, size_t i, float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Partition states cross XCDs: system-scope accesses skip the per-XCD L2s.
+__device__ __forceinline__ void publish(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ float collect(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // Running-state sentinel: finite, so exp2(sentinel - sentinel) = 1 for rows
 // that have seen no token yet (their sum and output are still zero).
 constexpr float kNoMax = -1.0e30f;
@@ -141,7 +156,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave index is the same on every lane; say so, so loops over it stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Hkv = a.num_kv_heads;
 
   const int ctx = a.context_lens[b];
@@ -295,44 +311,84 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     if (nparts == 1) {
       store_out(DT{}, a.out, out_base + e, A / L);
     } else {
-      a.ws_acc[part_base * D + e] = A;
+      publish(a.ws_acc + part_base * D + e, A);
       if (d == 0) {
-        a.ws_ml[(part_base + hh) * 2 + 0] = M;
-        a.ws_ml[(part_base + hh) * 2 + 1] = L;
+        publish(a.ws_ml + (part_base + hh) * 2 + 0, M);
+        publish(a.ws_ml + (part_base + hh) * 2 + 1, L);
       }
     }
   }
   if (nparts == 1) return;
 
-  // Publish this partition; the last arrival merges all of them.
-  __threadfence();
+  // Count this partition in once all of its stores have completed; the
+  // workgroup that brings the count to nparts merges.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const int prev = __hip_atomic_fetch_add(a.ws_count + bg, 1, __ATOMIC_ACQ_REL,
-                                            __HIP_MEMORY_SCOPE_AGENT);
+    const int prev = __hip_atomic_fetch_add(a.counters + bg, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_SYSTEM);
     s_last = (prev == nparts - 1);
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
+  // Merge: partition maxima and sums go through LDS in chunks of up to 64
+  // partitions (one system-scope load per value); each thread keeps a
+  // running (max, sum, output) for the elements it owns and rescales it
+  // when a chunk raises the maximum.  Chunks and partitions are visited in
+  // index order, so the result does not depend on arrival order.
+  constexpr int kChunk = 64;
+  constexpr int EPT = (G * D + NT - 1) / NT;  // elements per thread
+  __shared__ float s_pm[kChunk][G];
+  __shared__ float s_pl[kChunk][G];
   const size_t seq_base = bg * a.max_parts * (size_t)G;
-  for (int e = tid; e < G * D; e += NT) {
-    const int hh = e / D;
-    float M = kNoMax;
-    for (int pp = 0; pp < nparts; ++pp)
-      M = fmaxf(M, a.ws_ml[(seq_base + (size_t)pp * G + hh) * 2]);
-    float L = 0.0f, A = 0.0f;
-    for (int pp = 0; pp < nparts; ++pp) {
-      const size_t r = seq_base + (size_t)pp * G + hh;
-      const float f = fast_exp2(a.ws_ml[r * 2] - M);
-      L += a.ws_ml[r * 2 + 1] * f;
-      A += a.ws_acc[(seq_base + (size_t)pp * G) * D + e] * f;
+  float rM[EPT], rL[EPT], rA[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    rM[k] = kNoMax;
+    rL[k] = 0.0f;
+    rA[k] = 0.0f;
+  }
+  for (int c0 = 0; c0 < nparts; c0 += kChunk) {
+    const int n = min(kChunk, nparts - c0);
+    for (int i = tid; i < n * G; i += NT) {
+      const int pp = i / G, hh = i % G;
+      const size_t r = seq_base + (size_t)(c0 + pp) * G + hh;
+      s_pm[pp][hh] = collect(a.ws_ml + r * 2);
+      s_pl[pp][hh] = collect(a.ws_ml + r * 2 + 1);
     }
-    store_out(DT{}, a.out, out_base + e, A / L);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int e = tid + k * NT;
+      if (EPT * NT == G * D || e < G * D) {
+        const int hh = e / D;
+        float M = rM[k];
+        for (int pp = 0; pp < n; ++pp) M = fmaxf(M, s_pm[pp][hh]);
+        const float f0 = fast_exp2(rM[k] - M);
+        float L = rL[k] * f0, A = rA[k] * f0;
+        const float* acc_p = a.ws_acc + (seq_base + (size_t)c0 * G) * D + e;
+#pragma unroll 8
+        for (int pp = 0; pp < n; ++pp) {
+          const float f = fast_exp2(s_pm[pp][hh] - M);
+          L += s_pl[pp][hh] * f;
+          A += collect(acc_p + (size_t)pp * G * D) * f;
+        }
+        rM[k] = M;
+        rL[k] = L;
+        rA[k] = A;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = tid + k * NT;
+    if (EPT * NT == G * D || e < G * D) store_out(DT{}, a.out, out_base + e, rA[k] / rL[k]);
   }
   if (tid == 0)
-    __hip_atomic_store(a.ws_count + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.counters + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // ------------------------------------------------------------------ host
@@ -343,7 +399,7 @@ constexpr int kWaves = 4;
 struct Geometry {
   int part_blocks;
   int max_parts;
-  size_t acc_bytes, ml_bytes, count_bytes, total;
+  size_t acc_bytes, ml_bytes, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -383,14 +439,13 @@ bool geometry(int B, int Hq, int Hkv, int D, int max_blocks, int bs, int request
   out->part_blocks = pb;
   out->max_parts = (max_blocks + pb - 1) / pb;
   if (out->max_parts <= 1 || B == 0) {
-    out->acc_bytes = out->ml_bytes = out->count_bytes = out->total = 0;
+    out->acc_bytes = out->ml_bytes = out->total = 0;
     return true;
   }
   const size_t rows = (size_t)B * Hkv * out->max_parts * (size_t)(Hq / Hkv);
   out->acc_bytes = align256(rows * D * sizeof(float));
   out->ml_bytes = align256(rows * 2 * sizeof(float));
-  out->count_bytes = align256((size_t)B * Hkv * sizeof(int32_t));
-  out->total = out->acc_bytes + out->ml_bytes + out->count_bytes;
+  out->total = out->acc_bytes + out->ml_bytes;
   return true;
 }
 
@@ -457,8 +512,8 @@ extern "C" pa_status pa_paged_attention_decode(
     const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
     int32_t block_size, int32_t max_blocks_per_seq, float scale,
-    int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
-    void* stream) {
+    int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* counters,
+    int64_t num_counters, pa_dtype dtype, void* stream) {
   clear_error();
   if (!supported_dtype(dtype)) {
     set_error("dtype %d is not PA_DTYPE_F32 or PA_DTYPE_BF16", (int)dtype);
@@ -522,6 +577,11 @@ extern "C" pa_status pa_paged_attention_decode(
       set_error("workspace must be non-NULL and 256-byte aligned");
       return PA_ERR_INVALID_ARGUMENT;
     }
+    if (!counters || num_counters < (int64_t)num_seqs * num_kv_heads) {
+      set_error("counters must hold num_seqs * num_kv_heads = %lld int32 (got %lld)",
+                (long long)num_seqs * num_kv_heads, (long long)num_counters);
+      return PA_ERR_WORKSPACE_TOO_SMALL;
+    }
   }
 
   DecodeArgs a;
@@ -534,8 +594,7 @@ extern "C" pa_status pa_paged_attention_decode(
   char* ws = static_cast<char*>(workspace);
   a.ws_acc = geo.total ? reinterpret_cast<float*>(ws) : nullptr;
   a.ws_ml = geo.total ? reinterpret_cast<float*>(ws + geo.acc_bytes) : nullptr;
-  a.ws_count = geo.total ? reinterpret_cast<int32_t*>(ws + geo.acc_bytes + geo.ml_bytes)
-                         : nullptr;
+  a.counters = geo.total ? counters : nullptr;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.num_blocks = num_blocks;

@@ -52,12 +52,12 @@ def test_status_strings(lib):
 
 def _decode(lib, **kw):
     a = dict(out=16, q=16, k=16, v=16, bt=16, cl=16, B=4, Hq=4, Hkv=2, D=64, nb=32,
-             bs=16, mb=4, scale=0.125, ps=0, ws=None, wsb=0, dt=0)
+             bs=16, mb=4, scale=0.125, ps=0, ws=None, wsb=0, cnt=None, ncnt=0, dt=0)
     a.update(kw)
     return lib.pa_paged_attention_decode(
         a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["B"], a["Hq"], a["Hkv"],
         a["D"], a["nb"], a["bs"], a["mb"], a["scale"], a["ps"], a["ws"], a["wsb"],
-        a["dt"], None)
+        a["cnt"], a["ncnt"], a["dt"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -74,6 +74,9 @@ def _decode(lib, **kw):
     (dict(q=None), INVALID),
     (dict(k=8), INVALID),                   # misaligned
     (dict(mb=400, ps=16), WS_SMALL),        # needs partials, none given
+    (dict(mb=400, ps=16, ws=256, wsb=1 << 30), WS_SMALL),  # no counters
+    (dict(mb=400, ps=16, ws=256, wsb=1 << 30, cnt=256, ncnt=7), WS_SMALL),
+    (dict(mb=400, ps=16, ws=128, wsb=1 << 30, cnt=256, ncnt=8), INVALID),
     (dict(B=0, q=None, out=None), OK),      # empty batch: nothing to do
 ])
 def test_decode_argument_checks(lib, kw, status):
@@ -117,14 +120,14 @@ def test_workspace_size_rule(lib):
     # no workspace when every sequence fits one partition
     assert pa.decode_workspace_bytes(4, 4, 2, 64, 4, 16, 64) == 0
     # otherwise: G*D floats of output + 2 floats per (seq, kv head, partition,
-    # head), plus one int32 counter per (seq, kv head), each 256-byte aligned
+    # head), each region 256-byte aligned (the counters are a separate array)
     B, Hq, Hkv, D, mb, bs, ps = 8, 32, 8, 128, 2048, 16, 512
     parts = mb * bs // ps
     rows = B * Hkv * parts * (Hq // Hkv)
 
     def al(x):
         return (x + 255) // 256 * 256
-    want = al(rows * D * 4) + al(rows * 2 * 4) + al(B * Hkv * 4)
+    want = al(rows * D * 4) + al(rows * 2 * 4)
     assert pa.decode_workspace_bytes(B, Hq, Hkv, D, mb, bs, ps) == want
     assert pa.decode_workspace_bytes(B, Hq, Hkv, D, mb, bs, 24) == 0  # invalid
 
@@ -149,6 +152,6 @@ def test_one_hip_runtime_in_process(lib):
 
 def test_ctypes_signatures_match_header(lib):
     assert lib.pa_decode_workspace_bytes.restype is ctypes.c_size_t
-    assert len(lib.pa_paged_attention_decode.argtypes) == 19
+    assert len(lib.pa_paged_attention_decode.argtypes) == 21
     assert len(lib.pa_reshape_and_cache.argtypes) == 12
     assert len(lib.pa_debug_gather_kv.argtypes) == 14

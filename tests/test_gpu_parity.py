@@ -320,3 +320,27 @@ def test_side_stream_and_given_out():
                                   d["context_lens"], d["scale"], out=out)
     s.synchronize()
     assert np.array_equal(G.host_storage(out), base)
+
+
+def test_one_counter_array_serves_every_geometry():
+    """Counters left at zero by each call: alternate two geometries whose
+    partial results overlap differently, with one shared counter array."""
+    cnt = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    cases = [("qwen3_0p6b", 64), ("bf16_d128_bs16_g16", 32), ("llama32_1b", 128),
+             ("qwen3_0p6b", 32)]
+    for name, ps in cases:
+        inp = inputs_for(name)
+        w = inp["workload"]
+        say("decode shared counters", name, ps)
+        d = G.upload(inp)
+        pa.reshape_and_cache(d["key"], d["value"], d["k_cache"], d["v_cache"],
+                             d["slot_mapping"])
+        need = pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                                         w.head_dim, inp["max_blocks"], w.block_size, ps)
+        ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")  # junk
+        out = pa.paged_attention_decode(d["q"], d["k_cache"], d["v_cache"],
+                                        d["block_tables"], d["context_lens"], d["scale"],
+                                        partition_size=ps, workspace=ws, counters=cnt)
+        ref, _ = oracle_step(inp)
+        G.assert_close(G.host_f64(out), ref, w.dtype, f"{name} ps={ps}")
+        assert int(cnt.abs().sum()) == 0
