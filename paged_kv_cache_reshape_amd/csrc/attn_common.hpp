@@ -1,0 +1,328 @@
+// Pieces shared by the decode kernels: the lane layout of a KV row, the
+// per-row online-softmax state, cross-XCD publishing of partial states, and
+// the log-sum-exp merge of partial states.
+//
+// What is computed (barellm README, feature list and paged-cache list;
+// LLAISYS README, self-attention item): for sequence b and query head h,
+// softmax attention of q[b,h] over the first context_lens[b] cached rows of KV
+// head h / G, the rows found through the block table; float32 accumulation;
+// softmax in running max / running sum form (online softmax).
+#pragma once
+
+#include "common.hpp"
+
+#include <math.h>
+
+namespace pa {
+
+// Everything a decode kernel receives.  Workspace regions are laid out by the
+// host for the kernel that runs.
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_acc;      // unnormalised partial outputs
+  float* ws_ml;       // (max, sum) of each partial state, base-2 units
+  int32_t* counters;  // arrivals per merged unit, reset by the merger
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t max_blocks;
+  int32_t part_blocks;   // partition kernel: blocks per partition
+  int32_t max_parts;     // partition kernel: partitions per sequence, at most
+  int32_t heads_per_wg;  // consecutive kv heads one workgroup takes (1, 2 or 4)
+  float scale_log2;      // scale * log2(e): scores are kept in base-2 units
+};
+
+// Lane layout.  One KV row (one token, one kv head) is D*elt contiguous bytes
+// spread over RL lanes of 16 bytes; a wave load covers ROWS rows; a block of
+// BS tokens takes NI loads for K and NI for V.  A wave serves GW query heads
+// of one kv head; groups larger than 8 are split over HS waves.
+template <class DT, int D, int BS, int G, int NW>
+struct DecodeShape {
+  static constexpr int E = DT::kPerChunk;
+  static constexpr int RL = D / E;
+  static constexpr int ROWS = 64 / RL;
+  static constexpr int NI = BS / ROWS;
+  static constexpr int GW = G < 8 ? G : 8;
+  static constexpr int HS = G / GW;
+  static constexpr int MAX_HPW = (NW / HS) < 4 ? (NW / HS) : 4;
+  static constexpr int GH = G * MAX_HPW;  // query heads of a workgroup, at most
+  static_assert(RL >= 4 && RL <= 32, "row must span 4..32 lanes");
+  static_assert(BS % ROWS == 0, "block must be whole wave loads");
+  static_assert(NW % HS == 0, "waves must cover every head split");
+};
+
+// q.k over one 16-byte chunk, float32 accumulation (bf16 products are exact).
+__device__ __forceinline__ float chunk_dot(BF16, uint4 q, uint4 k) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.x),
+                                            __builtin_bit_cast(bf16x2, k.x), 0.0f, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.y),
+                                      __builtin_bit_cast(bf16x2, k.y), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.z),
+                                      __builtin_bit_cast(bf16x2, k.z), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.w),
+                                      __builtin_bit_cast(bf16x2, k.w), s, false);
+  return s;
+}
+__device__ __forceinline__ float chunk_dot(F32, uint4 q, uint4 k) {
+  float s = __uint_as_float(q.x) * __uint_as_float(k.x);
+  s = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), s);
+  s = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), s);
+  s = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), s);
+  return s;
+}
+
+__device__ __forceinline__ void unpack(BF16, uint4 v, float* f) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+__device__ __forceinline__ void unpack(F32, uint4 v, float* f) {
+  f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+  f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+}
+
+__device__ __forceinline__ void store_out(BF16, void* base, size_t i, float x) {
+  static_cast<uint16_t*>(base)[i] = f32_to_bf16_rne(x);
+}
+__device__ __forceinline__ void store_out(F32, void* base, size_t i, float x) {
+  static_cast<float*>(base)[i] = x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Partial states cross XCDs, and MI355X's per-XCD L2s are not coherent with
+// each other.  A device-scope fence would write back and invalidate the whole
+// L2 of the XCD; instead partial states are stored and loaded with
+// system-scope atomic accesses, which go around the L2s.
+__device__ __forceinline__ void publish(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ float collect(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Running-state sentinel: finite, so exp2(sentinel - sentinel) = 1 for rows
+// that have seen no token yet (their sum and output are still zero).
+constexpr float kNoMax = -1.0e30f;
+
+// Online-softmax state of one wave for GW query heads of one kv head.  Each
+// row of the wave (RL lanes) keeps its own (max, sum, output slice) over the
+// tokens it saw; rows are merged once at the end with lane swaps.
+template <class DT, int D, int BS, int G, int NW>
+struct RowAttn {
+  using Sh = DecodeShape<DT, D, BS, G, NW>;
+  using S = typename DT::storage;
+  static constexpr int E = Sh::E, RL = Sh::RL, ROWS = Sh::ROWS, NI = Sh::NI;
+  static constexpr int GW = Sh::GW;
+
+  float m[GW], l[GW], acc[GW][E];
+  uint4 qv[GW];
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int h = 0; h < GW; ++h) {
+      m[h] = kNoMax;
+      l[h] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[h][e] = 0.0f;
+    }
+  }
+
+  // q rows of GW consecutive query heads starting at `q_head0` (an element
+  // pointer to q[b, h0, 0]); this lane's 16-byte slice of each.
+  __device__ __forceinline__ void load_q(const S* q_head0, int col) {
+#pragma unroll
+    for (int h = 0; h < GW; ++h) qv[h] = load_chunk(q_head0 + (size_t)h * D + col * E);
+  }
+
+  // K and V rows of one block: kb / vb point at this lane's chunk of the
+  // block's first row for this kv head; rows are tok_stride elements apart.
+  __device__ __forceinline__ static void fetch(const S* kb, const S* vb, size_t tok_stride,
+                                               uint4 (&kr)[NI], uint4 (&vr)[NI]) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) kr[i] = load_chunk(kb + (size_t)i * ROWS * tok_stride);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) vr[i] = load_chunk(vb + (size_t)i * ROWS * tok_stride);
+  }
+
+  // Fold one block into the state.  pos0: sequence position of this lane's
+  // row in load 0; rows at or past ctx are masked (scores -inf, values 0, so
+  // anything stored there -- NaN included -- has no effect).
+  __device__ __forceinline__ void consume(int pos0, int ctx, bool full, float scale_log2,
+                                          const uint4 (&kr)[NI], const uint4 (&vr)[NI]) {
+    float s[NI][GW];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int h = 0; h < GW; ++h)
+        s[i][h] = group_sum<RL>(chunk_dot(DT{}, qv[h], kr[i])) * scale_log2;
+    if (!full) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        if (pos0 + i * ROWS >= ctx)
+#pragma unroll
+          for (int h = 0; h < GW; ++h) s[i][h] = -INFINITY;
+    }
+#pragma unroll
+    for (int h = 0; h < GW; ++h) {
+      float mx = m[h];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) mx = fmaxf(mx, s[i][h]);
+      const float alpha = fast_exp2(m[h] - mx);
+      m[h] = mx;
+      l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float vf[E];
+      unpack(DT{}, vr[i], vf);
+      if (!full && pos0 + i * ROWS >= ctx) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) vf[e] = 0.0f;
+      }
+#pragma unroll
+      for (int h = 0; h < GW; ++h) {
+        const float p = fast_exp2(s[i][h] - m[h]);
+        l[h] += p;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+      }
+    }
+  }
+
+  template <int kMask>
+  __device__ __forceinline__ void merge_step() {
+#pragma unroll
+    for (int h = 0; h < GW; ++h) {
+      const float mo = lane_xor<kMask>(m[h]);
+      const float lo = lane_xor<kMask>(l[h]);
+      const float M = fmaxf(m[h], mo);
+      const float sa = fast_exp2(m[h] - M);
+      const float sb = fast_exp2(mo - M);
+      l[h] = l[h] * sa + lo * sb;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float ao = lane_xor<kMask>(acc[h][e]);
+        acc[h][e] = acc[h][e] * sa + ao * sb;
+      }
+      m[h] = M;
+    }
+  }
+
+  // Rows of the wave -> one state, held by the lanes of row 0 (and the others).
+  __device__ __forceinline__ void merge_rows() {
+    if constexpr (RL <= 8) merge_step<8>();
+    if constexpr (RL <= 16) merge_step<16>();
+    merge_step<32>();
+  }
+
+  // Row 0 writes the wave's state to LDS: acc[h][d], m[h], l[h].
+  __device__ __forceinline__ void to_lds(float (*s_acc)[D], float* s_m, float* s_l,
+                                         int lane) const {
+    if (lane < RL) {
+#pragma unroll
+      for (int h = 0; h < GW; ++h) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s_acc[h][lane * E + e] = acc[h][e];
+        if (lane == 0) {
+          s_m[h] = m[h];
+          s_l[h] = l[h];
+        }
+      }
+    }
+  }
+};
+
+// Merge stored partial states (m, l, acc) of one group of query heads into the
+// output.  `piece_rows(i)` returns the row index (into ws_ml / 2 and ws_acc /
+// D) of the first query head of piece i; rows of one piece are consecutive.
+// Pieces are read in index order through LDS in chunks of 64, so the result
+// does not depend on the order in which they were written.  Used by one whole
+// workgroup; `gh` query heads, D values each, output at out + out_base.
+template <class DT, int D, int GH, int NT, class RowFn>
+__device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int npieces, int gh,
+                                             RowFn piece_rows, size_t out_base,
+                                             float (*s_pm)[GH], float (*s_pl)[GH]) {
+  constexpr int kChunk = 64;
+  constexpr int EPT = (GH * D + NT - 1) / NT;  // output elements per thread, at most
+  const int tid = threadIdx.x;
+  const int elems = gh * D;
+  float rM[EPT], rL[EPT], rA[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    rM[k] = kNoMax;
+    rL[k] = 0.0f;
+    rA[k] = 0.0f;
+  }
+  for (int c0 = 0; c0 < npieces; c0 += kChunk) {
+    const int n = min(kChunk, npieces - c0);
+    for (int i = tid; i < n * gh; i += NT) {
+      const int pp = i / gh, qh = i % gh;
+      const size_t r = piece_rows(c0 + pp) + qh;
+      s_pm[pp][qh] = collect(a.ws_ml + r * 2);
+      s_pl[pp][qh] = collect(a.ws_ml + r * 2 + 1);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int e = tid + k * NT;
+      if (e < elems) {
+        const int qh = e / D, d = e % D;
+        float M = rM[k];
+        for (int pp = 0; pp < n; ++pp) M = fmaxf(M, s_pm[pp][qh]);
+        const float f0 = fast_exp2(rM[k] - M);
+        float L = rL[k] * f0, A = rA[k] * f0;
+#pragma unroll 8
+        for (int pp = 0; pp < n; ++pp) {
+          const float f = fast_exp2(s_pm[pp][qh] - M);
+          L += s_pl[pp][qh] * f;
+          A += collect(a.ws_acc + (piece_rows(c0 + pp) + qh) * D + d) * f;
+        }
+        rM[k] = M;
+        rL[k] = L;
+        rA[k] = A;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = tid + k * NT;
+    if (e < elems) store_out(DT{}, a.out, out_base + e, rA[k] / rL[k]);
+  }
+}
+
+// Publish-and-count: every thread's publish() stores must be complete before
+// the workgroup counts itself in; returns true in every thread of the
+// workgroup that brought the counter to `expected` (the merger), which also
+// finds the counter reset for the next call.
+__device__ __forceinline__ bool arrive(int32_t* counter, int expected, int* s_flag) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_SYSTEM);
+    *s_flag = (prev == expected - 1);
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+__device__ __forceinline__ void reset_counter(int32_t* counter) {
+  if (threadIdx.x == 0)
+    __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+}  // namespace pa

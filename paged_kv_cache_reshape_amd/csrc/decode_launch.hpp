@@ -1,0 +1,47 @@
+// Launch plumbing shared by the decode kernels: template dispatch over the
+// built shapes and the per-kernel launchers.
+#pragma once
+
+#include "attn_common.hpp"
+
+namespace pa {
+
+constexpr int kDecodeWaves = 4;       // waves per workgroup
+constexpr int kStreamKMaxSeqs = 4096; // per-sequence prefix sums live in LDS
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+// Calls f(dtype_tag, IntC<D>, IntC<BS>, IntC<G>) for the built combination.
+template <class F>
+hipError_t dispatch_decode(int dtype, int D, int BS, int G, F&& f) {
+  auto by_g = [&](auto dt, auto d, auto bs) -> hipError_t {
+    switch (G) {
+      case 1: return f(dt, d, bs, IntC<1>{});
+      case 2: return f(dt, d, bs, IntC<2>{});
+      case 4: return f(dt, d, bs, IntC<4>{});
+      case 8: return f(dt, d, bs, IntC<8>{});
+      case 16: return f(dt, d, bs, IntC<16>{});
+      case 32: return f(dt, d, bs, IntC<32>{});
+    }
+    return hipErrorInvalidValue;
+  };
+  auto by_bs = [&](auto dt, auto d) -> hipError_t {
+    return BS == 16 ? by_g(dt, d, IntC<16>{}) : by_g(dt, d, IntC<32>{});
+  };
+  auto by_d = [&](auto dt) -> hipError_t {
+    return D == 64 ? by_bs(dt, IntC<64>{}) : by_bs(dt, IntC<128>{});
+  };
+  return dtype == PA_DTYPE_BF16 ? by_d(BF16{}) : by_d(F32{});
+}
+
+hipError_t launch_partition(int dtype, int D, int BS, int G, const DecodeArgs& a,
+                            hipStream_t s);
+hipError_t launch_streamk(int dtype, int D, int BS, int G, const DecodeArgs& a,
+                          int num_wg, hipStream_t s);
+// Resident workgroups per compute unit of the balanced kernel (0 on error).
+int streamk_wgs_per_cu(int dtype, int D, int BS, int G);
+
+}  // namespace pa

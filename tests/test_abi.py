@@ -109,14 +109,26 @@ def test_partition_size_rule(lib):
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 500) == -1
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 64) == 1024
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 65) == -1
-    # the library's choice is a multiple of the block size, 4..64 blocks
+    # left to the library: the balanced schedule (reported as 0) up to 4096
+    # sequences, fixed partitions of 4..64 blocks beyond
     for args in [(32, 16, 8, 128, 128, 16), (64, 32, 8, 64, 256, 16),
                  (256, 32, 32, 128, 32, 32), (4, 4, 2, 64, 4, 16)]:
-        p = pa.decode_partition_size(*args, 0)
-        assert p % args[-1] == 0 and 4 <= p // args[-1] <= 64
+        assert pa.decode_partition_size(*args, 0) == 0
+    p = pa.decode_partition_size(5000, 16, 8, 128, 128, 16, 0)
+    assert p % 16 == 0 and 4 <= p // 16 <= 64
 
 
 def test_workspace_size_rule(lib):
+    # balanced schedule: two partial states per workgroup, workgroups = compute
+    # units x resident workgroups per unit (no GPU here: 256 units, and the
+    # fallback of 4 per unit)
+    B, Hq, Hkv, D, mb, bs = 32, 16, 8, 128, 128, 16
+    got = pa.decode_workspace_bytes(B, Hq, Hkv, D, mb, bs, 0)
+    rows = 256 * 4 * 2 * 4 * 2  # wgs * pieces * kv heads per wg * G
+
+    def al(x):
+        return (x + 255) // 256 * 256
+    assert got == al(rows * D * 4) + al(rows * 2 * 4)
     # no workspace when every sequence fits one partition
     assert pa.decode_workspace_bytes(4, 4, 2, 64, 4, 16, 64) == 0
     # otherwise: G*D floats of output + 2 floats per (seq, kv head, partition,
