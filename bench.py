@@ -38,7 +38,9 @@ import synth  # noqa: E402
 METRIC = "decode-attention KV GB/s and % of HBM peak; µs/step at B=32 Qwen3-0.6B shape"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_reshape_amd", "csrc", "decode.hip")
+DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_reshape_amd", "csrc", f)
+               for f in ("decode_partition.hip", "attn_common.hpp", "common.hpp",
+                         "decode_launch.hpp", "decode_api.hip")]
 
 
 def algorithmic_bytes(inp: dict) -> dict:
@@ -60,12 +62,20 @@ def traffic_record():
     they were taken on the decode kernel as it is now (source hash matches)."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
-        src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
     except (OSError, ValueError):
         return None
-    if rec.get("decode_hip_sha256") != src:
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
         return None
     return rec
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the decode kernel's sources, in a fixed order."""
+    h = hashlib.sha256()
+    for path in DECODE_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def cpu_baseline(inp: dict, budget_s: float) -> dict:
@@ -141,7 +151,9 @@ def main() -> int:
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     pool_bytes = 2 * inp["k_cache"].nbytes
-    R = args.replicas or max(1, math.ceil(1.25 * 2**30 / pool_bytes))
+    # Enough pool copies that one pass over them (1.25 GiB) cannot sit in the
+    # caches; at most 64 (tiny pools are launch-bound anyway).
+    R = args.replicas or min(64, max(1, math.ceil(1.25 * 2**30 / pool_bytes)))
     kc0, vc0 = up(inp["k_cache"]), up(inp["v_cache"])
     kcs = [kc0] + [kc0.clone() for _ in range(R - 1)]
     vcs = [vc0] + [vc0.clone() for _ in range(R - 1)]
@@ -232,7 +244,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_kernel",
+            "kernel": "decode_partition_kernel",
             "bytes_per_launch": nbytes["decode"],
         },
     }

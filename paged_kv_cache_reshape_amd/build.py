@@ -25,8 +25,7 @@ LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 ARCH = "gfx950"
-HIP_SOURCES = ["decode_api.hip", "decode_partition.hip", "decode_streamk.hip",
-               "kv_write.hip"]
+HIP_SOURCES = ["decode_api.hip", "decode_partition.hip", "kv_write.hip"]
 HOST_SOURCES = ["status.cpp"]
 
 HIPCC_FLAGS = [

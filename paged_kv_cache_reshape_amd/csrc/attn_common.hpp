@@ -155,23 +155,24 @@ struct RowAttn {
   }
 
   // Fold one block into the state.  pos0: sequence position of this lane's
-  // row in load 0; rows at or past ctx are masked (scores -inf, values 0, so
-  // anything stored there -- NaN included -- has no effect).
-  __device__ __forceinline__ void consume(int pos0, int ctx, bool full, float scale_log2,
+  // row in load 0; rows at or past ctx, and every row when `live` is false,
+  // are masked (score -inf, value bits 0,
+  // so anything stored there -- NaN included -- has no effect).  The masking
+  // is branch-free: a branch here would give the compiler paths with
+  // different loads outstanding, and it would then wait for all of them.
+  __device__ __forceinline__ void consume(int pos0, int ctx, bool live, float scale_log2,
                                           const uint4 (&kr)[NI], const uint4 (&vr)[NI]) {
+    bool valid[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) valid[i] = live && pos0 + i * ROWS < ctx;
     float s[NI][GW];
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int h = 0; h < GW; ++h)
-        s[i][h] = group_sum<RL>(chunk_dot(DT{}, qv[h], kr[i])) * scale_log2;
-    if (!full) {
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-        if (pos0 + i * ROWS >= ctx)
-#pragma unroll
-          for (int h = 0; h < GW; ++h) s[i][h] = -INFINITY;
-    }
+      for (int h = 0; h < GW; ++h) {
+        const float x = group_sum<RL>(chunk_dot(DT{}, qv[h], kr[i])) * scale_log2;
+        s[i][h] = valid[i] ? x : -INFINITY;
+      }
 #pragma unroll
     for (int h = 0; h < GW; ++h) {
       float mx = m[h];
@@ -185,12 +186,10 @@ struct RowAttn {
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      const uint4 vb = valid[i] ? vr[i] : z;
       float vf[E];
-      unpack(DT{}, vr[i], vf);
-      if (!full && pos0 + i * ROWS >= ctx) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) vf[e] = 0.0f;
-      }
+      unpack(DT{}, vb, vf);
 #pragma unroll
       for (int h = 0; h < GW; ++h) {
         const float p = fast_exp2(s[i][h] - m[h]);
@@ -243,6 +242,46 @@ struct RowAttn {
     }
   }
 };
+
+// Blocks a wave keeps in flight while it consumes one.  Throughput follows
+// the bytes outstanding per compute unit, and registers are the largest
+// buffer a wave has (a block of K and V rows for one kv head is 32 VGPRs at
+// head_dim 128 in bf16), so the pipeline is PF blocks deep.  Measured on
+// MI355X (Qwen3-shaped batch): depth 2 beats 3, 4 and 5, whose extra
+// registers cost more occupancy than the extra depth returns.
+#ifndef PA_PREFETCH_DEPTH
+#define PA_PREFETCH_DEPTH 2
+#endif
+
+// Walk blocks jj = first, first + step, ... < n with the next PF-1 blocks'
+// loads in flight while the current one is consumed.  Written so that the
+// compiler keeps that overlap: the loop body has no branch (a block index at
+// or past n is fetched as block n-1, which is in bounds, and consumed with
+// every row masked), the ring of PF buffers is indexed with constants only
+// (the loop is unrolled by PF), and a scheduling barrier keeps each prefetch
+// issued ahead of the arithmetic that does not need it.
+template <int NI, class Fetch, class Consume>
+__device__ __forceinline__ void stream_blocks(int first, int step, int n, Fetch&& fetch,
+                                              Consume&& consume) {
+  constexpr int PF = PA_PREFETCH_DEPTH;
+  if (first >= n) return;
+  auto clamp = [&](int j) { return j < n ? j : n - 1; };
+  uint4 kr[PF][NI], vr[PF][NI];
+#pragma unroll
+  for (int p = 0; p < PF - 1; ++p) {
+    fetch(clamp(first + p * step), kr[p], vr[p]);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads of one block together
+  }
+  for (int jj = first; jj < n; jj += PF * step) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      fetch(clamp(jj + (u + PF - 1) * step), kr[(u + PF - 1) % PF], vr[(u + PF - 1) % PF]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int j = jj + u * step;
+      consume(j, j < n, kr[u], vr[u]);
+    }
+  }
+}
 
 // Merge stored partial states (m, l, acc) of one group of query heads into the
 // output.  `piece_rows(i)` returns the row index (into ws_ml / 2 and ws_acc /

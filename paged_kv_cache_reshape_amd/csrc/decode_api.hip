@@ -1,14 +1,11 @@
 // C ABI of the decode: argument checks, the choice of schedule, workspace
 // layout and the launch.
 //
-// Two schedules compute the same function (the kernels' headers describe
-// them):
-//   * balanced ("stream-K"): equal shares of the batch's (sequence, kv-head
-//     group, block) units for a grid that fills the GPU -- used when the
-//     caller leaves the partition size to the library (partition_size 0);
-//   * fixed partitions: partition_size tokens per workgroup -- used when the
-//     caller names a partition size, and for batches too large for the
-//     balanced kernel's per-sequence table in LDS.
+// The decode runs as fixed partitions (decode_partition.hip): one workgroup per
+// (kv-head group, sequence, partition of partition_size tokens).  When the
+// caller leaves the partition size to the library it picks, by shape, the
+// partition length and the kv heads per workgroup that measured fastest on
+// MI355X for the decode workloads (see auto_partition_tokens).
 #include "decode_launch.hpp"
 
 #include <stdlib.h>
@@ -22,99 +19,51 @@ bool group_supported(int g) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Consecutive kv heads one workgroup takes: up to 4, so that the workgroup's
-// waves read neighbouring rows of each token (one contiguous run of
-// hpw * head_dim elements) together; fewer when large query-head groups
-// already need the waves.
-int heads_per_workgroup(int Hkv, int G) {
+// Consecutive kv heads one workgroup takes: its waves then read neighbouring
+// rows of each token (one contiguous run of hpw * head_dim elements) together.
+//
+// Measured: two heads per workgroup at head_dim 128, one at head_dim 64 (whose
+// 128-byte rows already fill a load with eight tokens).  PAGEDATTN_HEADS_PER_WG
+// overrides the choice (1, 2 or 4) for experiments.
+int heads_per_workgroup(int Hkv, int G, int D) {
   const int hs = G > 8 ? G / 8 : 1;
   if (const char* env = getenv("PAGEDATTN_HEADS_PER_WG")) {
     const int v = atoi(env);
     if ((v == 1 || v == 2 || v == 4) && Hkv % v == 0 && v * hs <= kDecodeWaves) return v;
   }
-  for (int h = 4; h > 1; h /= 2)
-    if (Hkv % h == 0 && h * hs <= kDecodeWaves) return h;
+  if (D == 128 && Hkv % 2 == 0 && 2 * hs <= kDecodeWaves) return 2;
   return 1;
 }
 
-// Compute units of the current device (cached); 256 (MI355X) if unknown.
-int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
-// Workgroups of the balanced schedule: every compute unit filled to its
-// resident limit (an environment override exists for tuning).
-int streamk_grid(int dtype, int D, int BS, int G) {
-  int per_cu = 0;
-  if (const char* env = getenv("PAGEDATTN_WGS_PER_CU")) per_cu = atoi(env);
-  if (per_cu <= 0) per_cu = streamk_wgs_per_cu(dtype, D, BS, G);
-  if (per_cu <= 0) per_cu = 4;
-  return device_cus() * per_cu;
-}
-
-int auto_part_blocks(int B, int Hkv, int max_blocks) {
-  const long target = 8L * 256;
-  int pb = kMaxPartitionBlocks;
-  while (pb > 4) {
-    const long parts = (max_blocks + pb - 1) / pb;
-    if ((long)B * Hkv * parts >= target) break;
-    pb /= 2;
-  }
-  return pb;
-}
+// Library choice of partition length.  Measured on MI355X over the decode
+// workloads (Qwen3-, Llama-3.2-shaped, long-context, large-batch MHA/MQA):
+// long partitions win -- few workgroups streaming about 1 MB each keep every
+// compute unit's queue of outstanding loads full, and fewer sequences need a
+// merge -- except at head_dim 64, where 512 tokens is better.
+int auto_partition_tokens(int D) { return D == 128 ? 1024 : 512; }
 
 struct Plan {
-  bool streamk;
-  int part_blocks;  // fixed partitions
+  int part_blocks;
   int max_parts;
-  int num_wg;       // balanced
   int hpw;
   size_t acc_bytes, ml_bytes, total;
 };
 
-// The schedule and workspace for these sizes; false if `requested` is invalid.
-bool make_plan(int dtype, int B, int Hq, int Hkv, int D, int max_blocks, int bs,
-               int requested, Plan* p) {
+// The partitioning and workspace for these sizes; false if invalid.
+bool make_plan(int B, int Hq, int Hkv, int D, int max_blocks, int bs, int requested,
+               Plan* p) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || max_blocks <= 0) return false;
   if (!supported_head_dim(D) || !supported_block_size(bs)) return false;
   const int G = Hq / Hkv;
   if (!group_supported(G)) return false;
-  p->hpw = heads_per_workgroup(Hkv, G);
-  p->acc_bytes = p->ml_bytes = p->total = 0;
-  p->num_wg = 0;
-  p->part_blocks = 0;
-  p->max_parts = 0;
-  if (requested == 0 && B <= kStreamKMaxSeqs) {
-    p->streamk = true;
-    if (B == 0) return true;
-    p->num_wg = streamk_grid(dtype, D, bs, G);
-    const size_t rows = (size_t)p->num_wg * 2 * p->hpw * G;
-    p->acc_bytes = align256(rows * D * sizeof(float));
-    p->ml_bytes = align256(rows * 2 * sizeof(float));
-    p->total = p->acc_bytes + p->ml_bytes;
-    return true;
-  }
-  p->streamk = false;
-  int pb;
-  if (requested == 0) {
-    pb = auto_part_blocks(B, Hkv, max_blocks);
-  } else {
-    if (requested < 0 || requested % bs != 0) return false;
-    pb = requested / bs;
-    if (pb < 1 || pb > kMaxPartitionBlocks) return false;
-  }
+  p->hpw = heads_per_workgroup(Hkv, G, D);
+  const int tokens = requested == 0 ? auto_partition_tokens(D) : requested;
+  if (tokens < 0 || tokens % bs != 0) return false;
+  const int pb = tokens / bs;
+  if (pb < 1 || pb > kMaxPartitionBlocks) return false;
   p->part_blocks = pb;
   p->max_parts = (max_blocks + pb - 1) / pb;
+  p->acc_bytes = p->ml_bytes = p->total = 0;
   if (p->max_parts <= 1 || B == 0) return true;
   const size_t rows = (size_t)B * Hkv * p->max_parts * G;
   p->acc_bytes = align256(rows * D * sizeof(float));
@@ -133,10 +82,10 @@ extern "C" int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_head
                                             int32_t max_blocks_per_seq,
                                             int32_t block_size, int32_t requested) {
   Plan p;
-  if (!make_plan(PA_DTYPE_BF16, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                 max_blocks_per_seq, block_size, requested, &p))
+  if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                 block_size, requested, &p))
     return -1;
-  return p.streamk ? 0 : p.part_blocks * block_size;
+  return p.part_blocks * block_size;
 }
 
 extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
@@ -144,15 +93,11 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
                                            int32_t max_blocks_per_seq,
                                            int32_t block_size,
                                            int32_t partition_size) {
-  // The balanced schedule's grid depends on the storage type's occupancy and
-  // this call does not name the type: size for the larger of the two.
-  Plan p16, p32;
-  if (!make_plan(PA_DTYPE_BF16, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                 max_blocks_per_seq, block_size, partition_size, &p16) ||
-      !make_plan(PA_DTYPE_F32, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                 max_blocks_per_seq, block_size, partition_size, &p32))
+  Plan p;
+  if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                 block_size, partition_size, &p))
     return 0;
-  return p16.total > p32.total ? p16.total : p32.total;
+  return p.total;
 }
 
 extern "C" pa_status pa_paged_attention_decode(
@@ -202,13 +147,13 @@ extern "C" pa_status pa_paged_attention_decode(
     return PA_ERR_INVALID_ARGUMENT;
   }
   Plan plan;
-  if (!make_plan(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+  if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
                  block_size, partition_size, &plan)) {
     set_error("partition_size=%d must be 0 or a multiple of block_size=%d "
               "between 1 and 64 blocks", partition_size, block_size);
     return PA_ERR_INVALID_ARGUMENT;
   }
-  if (!plan.streamk && plan.max_parts > 65535) {
+  if (plan.max_parts > 65535) {
     set_error("%d partitions per sequence (max 65535): raise partition_size",
               plan.max_parts);
     return PA_ERR_UNSUPPORTED;
@@ -260,10 +205,7 @@ extern "C" pa_status pa_paged_attention_decode(
   a.scale_log2 = scale * 1.4426950408889634f;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t err =
-      plan.streamk
-          ? launch_streamk(dtype, head_dim, block_size, G, a, plan.num_wg, s)
-          : launch_partition(dtype, head_dim, block_size, G, a, s);
+  const hipError_t err = launch_partition(dtype, head_dim, block_size, G, a, s);
   if (err != hipSuccess) {
     set_error("decode launch failed: %s", hipGetErrorString(err));
     return PA_ERR_HIP;

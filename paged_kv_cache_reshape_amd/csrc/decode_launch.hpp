@@ -7,7 +7,6 @@
 namespace pa {
 
 constexpr int kDecodeWaves = 4;       // waves per workgroup
-constexpr int kStreamKMaxSeqs = 4096; // per-sequence prefix sums live in LDS
 
 template <int V>
 struct IntC {
@@ -39,9 +38,6 @@ hipError_t dispatch_decode(int dtype, int D, int BS, int G, F&& f) {
 
 hipError_t launch_partition(int dtype, int D, int BS, int G, const DecodeArgs& a,
                             hipStream_t s);
-hipError_t launch_streamk(int dtype, int D, int BS, int G, const DecodeArgs& a,
-                          int num_wg, hipStream_t s);
-// Resident workgroups per compute unit of the balanced kernel (0 on error).
-int streamk_wgs_per_cu(int dtype, int D, int BS, int G);
+
 
 }  // namespace pa

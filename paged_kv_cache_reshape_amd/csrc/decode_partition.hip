@@ -88,25 +88,11 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
     const size_t off = (size_t)__builtin_amdgcn_readlane(my_blk, j) * blk_stride;
     Row::fetch(kbase + off, vbase + off, tok_stride, kr, vr);
   };
-  auto consume = [&](int j, const uint4 (&kr)[NI], const uint4 (&vr)[NI]) {
-    st.consume((blk0 + j) * BS + row, ctx, (blk0 + j + 1) * BS <= ctx, a.scale_log2, kr, vr);
+  auto consume = [&](int j, bool live, const uint4 (&kr)[NI], const uint4 (&vr)[NI]) {
+    st.consume((blk0 + j) * BS + row, ctx, live, a.scale_log2, kr, vr);
   };
   // Two blocks in flight per wave.
-  {
-    uint4 kA[NI], vA[NI], kB[NI], vB[NI];
-    int j = tw;
-    if (j < nblk_run) fetch(j, kA, vA);
-    while (j < nblk_run) {
-      const int j1 = j + nwt;
-      if (j1 < nblk_run) fetch(j1, kB, vB);
-      consume(j, kA, vA);
-      if (j1 >= nblk_run) break;
-      const int j2 = j1 + nwt;
-      if (j2 < nblk_run) fetch(j2, kA, vA);
-      consume(j1, kB, vB);
-      j = j2;
-    }
-  }
+  stream_blocks<NI>(tw, nwt, nblk_run, fetch, consume);
   st.merge_rows();
 
   __shared__ float s_acc[NW][GW][D];

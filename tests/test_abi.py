@@ -109,26 +109,22 @@ def test_partition_size_rule(lib):
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 500) == -1
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 64) == 1024
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 65) == -1
-    # left to the library: the balanced schedule (reported as 0) up to 4096
-    # sequences, fixed partitions of 4..64 blocks beyond
-    for args in [(32, 16, 8, 128, 128, 16), (64, 32, 8, 64, 256, 16),
-                 (256, 32, 32, 128, 32, 32), (4, 4, 2, 64, 4, 16)]:
-        assert pa.decode_partition_size(*args, 0) == 0
-    p = pa.decode_partition_size(5000, 16, 8, 128, 128, 16, 0)
-    assert p % 16 == 0 and 4 <= p // 16 <= 64
+    # left to the library: 1024 tokens at head_dim 128, 512 at head_dim 64
+    assert pa.decode_partition_size(32, 16, 8, 128, 128, 16, 0) == 1024
+    assert pa.decode_partition_size(256, 32, 32, 128, 32, 32, 0) == 1024
+    assert pa.decode_partition_size(64, 32, 8, 64, 256, 16, 0) == 512
+    assert pa.decode_partition_size(4, 4, 2, 64, 4, 16, 0) == 512
 
 
 def test_workspace_size_rule(lib):
-    # balanced schedule: two partial states per workgroup, workgroups = compute
-    # units x resident workgroups per unit (no GPU here: 256 units, and the
-    # fallback of 4 per unit)
-    B, Hq, Hkv, D, mb, bs = 32, 16, 8, 128, 128, 16
-    got = pa.decode_workspace_bytes(B, Hq, Hkv, D, mb, bs, 0)
-    rows = 256 * 4 * 2 * 4 * 2  # wgs * pieces * kv heads per wg * G
-
     def al(x):
         return (x + 255) // 256 * 256
-    assert got == al(rows * D * 4) + al(rows * 2 * 4)
+    # library choice for the Qwen3 shape: 1024-token partitions of a
+    # 2048-token table -> 2 partitions per sequence
+    B, Hq, Hkv, D, mb, bs = 32, 16, 8, 128, 128, 16
+    rows = B * Hkv * 2 * (Hq // Hkv)
+    assert pa.decode_workspace_bytes(B, Hq, Hkv, D, mb, bs, 0) == \
+        al(rows * D * 4) + al(rows * 2 * 4)
     # no workspace when every sequence fits one partition
     assert pa.decode_workspace_bytes(4, 4, 2, 64, 4, 16, 64) == 0
     # otherwise: G*D floats of output + 2 floats per (seq, kv head, partition,
