@@ -39,8 +39,8 @@ METRIC = "decode-attention KV GB/s and % of HBM peak; µs/step at B=32 Qwen3-0.6
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_reshape_amd", "csrc", f)
-               for f in ("decode_partition.hip", "attn_common.hpp", "common.hpp",
-                         "decode_launch.hpp", "decode_api.hip")]
+               for f in ("decode_partition.hip", "decode_mfma.hip", "attn_common.hpp",
+                         "common.hpp", "decode_launch.hpp", "decode_api.hip")]
 
 
 def algorithmic_bytes(inp: dict) -> dict:

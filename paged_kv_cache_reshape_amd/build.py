@@ -25,7 +25,7 @@ LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 ARCH = "gfx950"
-HIP_SOURCES = ["decode_api.hip", "decode_partition.hip", "kv_write.hip"]
+HIP_SOURCES = ["decode_api.hip", "decode_partition.hip", "decode_mfma.hip", "kv_write.hip"]
 HOST_SOURCES = ["status.cpp"]
 
 HIPCC_FLAGS = [
@@ -59,30 +59,37 @@ def _run(cmd, verbose):
     return res
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every source and link ``libpagedattn.so``; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, jobs: int = 4, defines=(), out: str | None = None) -> str:
+    """Compile every source and link ``libpagedattn.so``; returns its path.
+
+    ``defines`` (``NAME=VALUE`` strings) and ``out`` build a variant of the
+    library elsewhere, in its own object folder, for tuning experiments.
+    """
+    lib_path = out or LIB_PATH
+    build_dir = BUILD_DIR if out is None else os.path.splitext(out)[0] + "_build"
+    os.makedirs(build_dir, exist_ok=True)
+    dflags = [f"-D{d}" for d in defines]
     hipcc = _hipcc()
     cmds = []
     objs = []
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD_DIR, src + ".o")
+        obj = os.path.join(build_dir, src + ".o")
         objs.append(obj)
-        cmds.append([hipcc, "-x", "hip", *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}",
+        cmds.append([hipcc, "-x", "hip", *HIPCC_FLAGS, *dflags, f"-I{INCLUDE}", f"-I{CSRC}",
                      "-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
-        obj = os.path.join(BUILD_DIR, src + ".o")
+        obj = os.path.join(build_dir, src + ".o")
         objs.append(obj)
         cmds.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}",
                      "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tlib = torch_lib_dir()
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     _run(["g++", "-shared", "-o", tmp, *objs, os.path.join(tlib, "libamdhip64.so"),
           f"-Wl,-rpath,{tlib}", "-Wl,--no-undefined", "-Wl,-z,defs"], verbose)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -50,8 +50,6 @@ struct DecodeShape {
   static constexpr int NI = BS / ROWS;
   static constexpr int GW = G < 8 ? G : 8;
   static constexpr int HS = G / GW;
-  static constexpr int MAX_HPW = (NW / HS) < 4 ? (NW / HS) : 4;
-  static constexpr int GH = G * MAX_HPW;  // query heads of a workgroup, at most
   static_assert(RL >= 4 && RL <= 32, "row must span 4..32 lanes");
   static_assert(BS % ROWS == 0, "block must be whole wave loads");
   static_assert(NW % HS == 0, "waves must cover every head split");
@@ -260,13 +258,12 @@ struct RowAttn {
 // every row masked), the ring of PF buffers is indexed with constants only
 // (the loop is unrolled by PF), and a scheduling barrier keeps each prefetch
 // issued ahead of the arithmetic that does not need it.
-template <int NI, class Fetch, class Consume>
+template <int NL, int PF = PA_PREFETCH_DEPTH, class Fetch, class Consume>
 __device__ __forceinline__ void stream_blocks(int first, int step, int n, Fetch&& fetch,
                                               Consume&& consume) {
-  constexpr int PF = PA_PREFETCH_DEPTH;
   if (first >= n) return;
   auto clamp = [&](int j) { return j < n ? j : n - 1; };
-  uint4 kr[PF][NI], vr[PF][NI];
+  uint4 kr[PF][NL], vr[PF][NL];
 #pragma unroll
   for (int p = 0; p < PF - 1; ++p) {
     fetch(clamp(first + p * step), kr[p], vr[p]);
@@ -289,48 +286,75 @@ __device__ __forceinline__ void stream_blocks(int first, int step, int n, Fetch&
 // Pieces are read in index order through LDS in chunks of 64, so the result
 // does not depend on the order in which they were written.  Used by one whole
 // workgroup; `gh` query heads, D values each, output at out + out_base.
+//
+// The partial outputs are read with system-scope loads, which go to memory:
+// every thread first issues the loads of U pieces for all its output
+// elements, then folds them in, so that U * EPT loads are in flight per
+// thread instead of one round trip per value.
 template <class DT, int D, int GH, int NT, class RowFn>
 __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int npieces, int gh,
                                              RowFn piece_rows, size_t out_base,
                                              float (*s_pm)[GH], float (*s_pl)[GH]) {
   constexpr int kChunk = 64;
   constexpr int EPT = (GH * D + NT - 1) / NT;  // output elements per thread, at most
+  constexpr int U = EPT >= 16 ? 1 : 16 / EPT;  // pieces whose loads are issued together
   const int tid = threadIdx.x;
   const int elems = gh * D;
   float rM[EPT], rL[EPT], rA[EPT];
+  int qh[EPT], dd[EPT];
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
     rM[k] = kNoMax;
     rL[k] = 0.0f;
     rA[k] = 0.0f;
+    const int e = min(tid + k * NT, elems - 1);  // threads past the end repeat the last
+    qh[k] = e / D;
+    dd[k] = e % D;
   }
+  float v[U][EPT];
+  // Partial outputs of pieces c0 + p0 .. c0 + p0 + U - 1 (clamped to the chunk).
+  auto load_batch = [&](int c0, int p0, int n) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t row = piece_rows(c0 + min(p0 + u, n - 1));
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) v[u][k] = collect(a.ws_acc + (row + qh[k]) * D + dd[k]);
+    }
+  };
   for (int c0 = 0; c0 < npieces; c0 += kChunk) {
     const int n = min(kChunk, npieces - c0);
+    // The first batch of partial outputs is requested with the chunk's
+    // (m, l) pairs: one memory round trip before anything can be folded.
+    load_batch(c0, 0, n);
     for (int i = tid; i < n * gh; i += NT) {
-      const int pp = i / gh, qh = i % gh;
-      const size_t r = piece_rows(c0 + pp) + qh;
-      s_pm[pp][qh] = collect(a.ws_ml + r * 2);
-      s_pl[pp][qh] = collect(a.ws_ml + r * 2 + 1);
+      const int pp = i / gh, h = i % gh;
+      const size_t r = piece_rows(c0 + pp) + h;
+      s_pm[pp][h] = collect(a.ws_ml + r * 2);
+      s_pl[pp][h] = collect(a.ws_ml + r * 2 + 1);
     }
     __syncthreads();
+    float M[EPT];
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
-      const int e = tid + k * NT;
-      if (e < elems) {
-        const int qh = e / D, d = e % D;
-        float M = rM[k];
-        for (int pp = 0; pp < n; ++pp) M = fmaxf(M, s_pm[pp][qh]);
-        const float f0 = fast_exp2(rM[k] - M);
-        float L = rL[k] * f0, A = rA[k] * f0;
-#pragma unroll 8
-        for (int pp = 0; pp < n; ++pp) {
-          const float f = fast_exp2(s_pm[pp][qh] - M);
-          L += s_pl[pp][qh] * f;
-          A += collect(a.ws_acc + (piece_rows(c0 + pp) + qh) * D + d) * f;
+      M[k] = rM[k];
+      for (int pp = 0; pp < n; ++pp) M[k] = fmaxf(M[k], s_pm[pp][qh[k]]);
+      const float f0 = fast_exp2(rM[k] - M[k]);
+      rL[k] *= f0;
+      rA[k] *= f0;
+      rM[k] = M[k];
+    }
+    for (int p0 = 0; p0 < n; p0 += U) {
+      if (p0 > 0) load_batch(c0, p0, n);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (p0 + u < n) {
+#pragma unroll
+          for (int k = 0; k < EPT; ++k) {
+            const float f = fast_exp2(s_pm[p0 + u][qh[k]] - M[k]);
+            rL[k] += s_pl[p0 + u][qh[k]] * f;
+            rA[k] += v[u][k] * f;
+          }
         }
-        rM[k] = M;
-        rL[k] = L;
-        rA[k] = A;
       }
     }
     __syncthreads();
@@ -362,6 +386,125 @@ __device__ __forceinline__ bool arrive(int32_t* counter, int expected, int* s_fl
 __device__ __forceinline__ void reset_counter(int32_t* counter) {
   if (threadIdx.x == 0)
     __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Where a partition workgroup stands: its sequence, kv-head group and
+// partition, the sequence's context length, this lane's block-table entry
+// (lane j holds the partition's block j), and how many blocks it streams.
+struct PartitionWork {
+  int b, gg, part, ctx, blk0, my_blk, nparts, nblk_run;
+  bool poisoned;
+};
+
+// Start of a partition workgroup (grid x = (kv-head group, sequence), y =
+// partition).  The context length, the block-table entries and -- through
+// `load_q` -- the query rows are requested together, before anything waits
+// on them.  Returns false when the workgroup has nothing to stream: its
+// partition starts past the context, or the context is empty (output zeros)
+// or out of range (output NaN), which the partition-0 workgroup writes.
+// Workgroups are dealt to the XCDs round-robin in linear-id order; with the
+// partition index slowest every partition index is spread over all XCDs.
+template <class DT, int D, int BS, int G, int NT, class LoadQ>
+__device__ __forceinline__ bool partition_prologue(const DecodeArgs& a, int lane,
+                                                   PartitionWork& w, LoadQ&& load_q) {
+  const int hpw = a.heads_per_wg;
+  const int n_groups = a.num_kv_heads / hpw;
+  w.gg = blockIdx.x % n_groups;
+  w.b = blockIdx.x / n_groups;
+  w.part = blockIdx.y;
+  w.ctx = a.context_lens[w.b];
+  w.blk0 = w.part * a.part_blocks;
+  const int32_t* trow = a.block_tables + (size_t)w.b * a.max_blocks + w.blk0;
+  w.my_blk = (lane < a.part_blocks && w.blk0 + lane < a.max_blocks) ? trow[lane] : 0;
+  load_q(w.b, w.gg);
+
+  const int part_tokens = a.part_blocks * BS;
+  const bool bad_ctx = w.ctx < 0 || w.ctx > a.max_blocks * BS;
+  w.nparts = (bad_ctx || w.ctx == 0) ? 1 : (w.ctx + part_tokens - 1) / part_tokens;
+  if (w.part >= w.nparts) return false;
+  if (bad_ctx || w.ctx == 0) {
+    const int wg_elems = hpw * G * D;
+    const size_t out_base = ((size_t)w.b * a.num_q_heads + (size_t)w.gg * hpw * G) * D;
+    const float fill = bad_ctx ? __builtin_nanf("") : 0.0f;
+    for (int e = threadIdx.x; e < wg_elems; e += NT) store_out(DT{}, a.out, out_base + e, fill);
+    return false;
+  }
+  const int nblk_seq = (w.ctx + BS - 1) / BS;
+  const int nblk = min(a.part_blocks, nblk_seq - w.blk0);
+  const bool bad_here = lane < nblk && (w.my_blk < 0 || w.my_blk >= a.num_blocks);
+  w.poisoned = __ballot(bad_here) != 0;  // same answer in every wave
+  w.nblk_run = w.poisoned ? 0 : nblk;
+  return true;
+}
+
+// End of a partition workgroup.  Every wave has left its state in LDS, one
+// slot per wave: wave w serves kv head w % hpw of the workgroup's group, head
+// slice (w / hpw) % HS and token share w / (hpw * HS).  The token shares of
+// each (kv head, query head) are combined; then the output is stored (the
+// sequence fits one partition), or the partial state is published and the
+// last workgroup of the (sequence, head group) to arrive merges every
+// partition into the output.
+template <class DT, int D, int G, int GW, int HS, int NW>
+__device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int gg, int part,
+                                                 int nparts, bool poisoned,
+                                                 const float (*s_acc)[GW][D],
+                                                 const float (*s_m)[GW],
+                                                 const float (*s_l)[GW]) {
+  constexpr int NT = NW * 64;
+  const int tid = threadIdx.x;
+  const int hpw = a.heads_per_wg;
+  const int Hkv = a.num_kv_heads;
+  const int n_groups = Hkv / hpw;
+  const int nwt = NW / (hpw * HS);  // waves sharing one (kv head, head slice)
+  const int wg_elems = hpw * G * D;
+  const size_t out_base = ((size_t)b * a.num_q_heads + (size_t)gg * hpw * G) * D;
+
+  for (int e = tid; e < wg_elems; e += NT) {
+    const int hwe = e / (G * D), rem = e % (G * D);
+    const int hh = rem / D, d = rem % D;
+    const int w0 = hwe + hpw * (hh / GW);
+    const int h = hh % GW;
+    float M = kNoMax;
+    for (int t = 0; t < nwt; ++t) M = fmaxf(M, s_m[w0 + hpw * HS * t][h]);
+    float L = 0.0f, A = 0.0f;
+    for (int t = 0; t < nwt; ++t) {
+      const int w = w0 + hpw * HS * t;
+      const float f = fast_exp2(s_m[w][h] - M);
+      L += s_l[w][h] * f;
+      A += s_acc[w][h][d] * f;
+    }
+    if (poisoned) L = __builtin_nanf("");
+    if (nparts == 1) {
+      store_out(DT{}, a.out, out_base + e, A / L);
+    } else {
+      const size_t pr = (((size_t)b * Hkv + gg * hpw + hwe) * a.max_parts + part) * G + hh;
+      publish(a.ws_acc + pr * D + d, A);
+      if (d == 0) {
+        publish(a.ws_ml + pr * 2 + 0, M);
+        publish(a.ws_ml + pr * 2 + 1, L);
+      }
+    }
+  }
+  if (nparts == 1) return;
+
+  __shared__ int s_last;
+  int32_t* counter = a.counters + (size_t)b * n_groups + gg;
+  if (!arrive(counter, nparts, &s_last)) return;
+
+  // Rows of partition p for query head qh of kv head x of the group: pieces
+  // of one kv head are max_parts * G rows apart, so merge one kv head at a
+  // time.
+  __shared__ float s_pm[64][G];
+  __shared__ float s_pl[64][G];
+  const size_t head_rows = (size_t)a.max_parts * G;
+  const size_t grp_base = ((size_t)b * Hkv + (size_t)gg * hpw) * head_rows;
+  for (int x = 0; x < hpw; ++x) {
+    const size_t base = grp_base + x * head_rows;
+    merge_pieces<DT, D, G, NT>(
+        a, nparts, G, [&](int p) { return base + (size_t)p * G; },
+        out_base + (size_t)x * G * D, s_pm, s_pl);
+  }
+  reset_counter(counter);
 }
 
 }  // namespace pa

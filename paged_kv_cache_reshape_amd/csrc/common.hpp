@@ -75,6 +75,17 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Maximum over aligned groups of kLanes lanes (kLanes in {4, 8, 16}).
+template <int kLanes>
+__device__ __forceinline__ float group_max(float x) {
+  static_assert(kLanes == 4 || kLanes == 8 || kLanes == 16, "");
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  if constexpr (kLanes >= 8) x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+  if constexpr (kLanes >= 16) x = fmaxf(x, dpp<kDppRowMirror>(x));
+  return x;
+}
+
 // Value of the lane whose index differs in bit `kMask` (kMask in {8,16,32}).
 template <int kMask>
 __device__ __forceinline__ float lane_xor(float x) {

@@ -1,14 +1,18 @@
-// C ABI of the decode: argument checks, the choice of schedule, workspace
-// layout and the launch.
+// C ABI of the decode: argument checks, the choice of kernel and schedule,
+// workspace layout and the launch.
 //
-// The decode runs as fixed partitions (decode_partition.hip): one workgroup per
-// (kv-head group, sequence, partition of partition_size tokens).  When the
+// The decode runs as fixed partitions: one workgroup per (kv-head group,
+// sequence, partition of partition_size tokens).  Two kernels share that
+// schedule, its workspace and its results: the matrix-core one
+// (decode_mfma.hip) for bfloat16 with 8, 16 or 32 query heads per kv head,
+// the vector-ALU one (decode_partition.hip) for everything else.  When the
 // caller leaves the partition size to the library it picks, by shape, the
 // partition length and the kv heads per workgroup that measured fastest on
 // MI355X for the decode workloads (see auto_partition_tokens).
 #include "decode_launch.hpp"
 
 #include <stdlib.h>
+#include <string.h>
 
 namespace pa {
 namespace {
@@ -41,6 +45,14 @@ int heads_per_workgroup(int Hkv, int G, int D) {
 // compute unit's queue of outstanding loads full, and fewer sequences need a
 // merge -- except at head_dim 64, where 512 tokens is better.
 int auto_partition_tokens(int D) { return D == 128 ? 1024 : 512; }
+
+// The matrix-core kernel where it applies.  PAGEDATTN_DECODE_KERNEL=valu
+// forces the vector-ALU kernel (tests compare the two).
+bool use_mfma(int dtype, int D, int bs, int G) {
+  if (!mfma_supported(dtype, D, bs, G)) return false;
+  const char* env = getenv("PAGEDATTN_DECODE_KERNEL");
+  return !(env && strcmp(env, "valu") == 0);
+}
 
 struct Plan {
   int part_blocks;
@@ -201,11 +213,15 @@ extern "C" pa_status pa_paged_attention_decode(
   a.max_blocks = max_blocks_per_seq;
   a.part_blocks = plan.part_blocks;
   a.max_parts = plan.max_parts;
-  a.heads_per_wg = plan.hpw;
+  const bool mfma = use_mfma(dtype, head_dim, block_size, G);
+  // The matrix-core kernel serves one kv head per workgroup (its eight waves
+  // split the blocks).
+  a.heads_per_wg = mfma ? 1 : plan.hpw;
   a.scale_log2 = scale * 1.4426950408889634f;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t err = launch_partition(dtype, head_dim, block_size, G, a, s);
+  const hipError_t err = mfma ? launch_mfma(head_dim, block_size, G, a, s)
+                             : launch_partition(dtype, head_dim, block_size, G, a, s);
   if (err != hipSuccess) {
     set_error("decode launch failed: %s", hipGetErrorString(err));
     return PA_ERR_HIP;

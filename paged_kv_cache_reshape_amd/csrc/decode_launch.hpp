@@ -6,7 +6,10 @@
 
 namespace pa {
 
-constexpr int kDecodeWaves = 4;       // waves per workgroup
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+constexpr int kDecodeWaves = PA_DECODE_WAVES;  // waves per workgroup
 
 template <int V>
 struct IntC {
@@ -38,6 +41,11 @@ hipError_t dispatch_decode(int dtype, int D, int BS, int G, F&& f) {
 
 hipError_t launch_partition(int dtype, int D, int BS, int G, const DecodeArgs& a,
                             hipStream_t s);
+
+// Matrix-core kernel for large query groups (bfloat16, G in {8, 16, 32}):
+// same arguments, workspace and results as launch_partition.
+bool mfma_supported(int dtype, int D, int BS, int G);
+hipError_t launch_mfma(int D, int BS, int G, const DecodeArgs& a, hipStream_t s);
 
 
 }  // namespace pa

@@ -32,6 +32,10 @@ EXTRA = {
                                       ("uniform", 1, 300), seed=34),
     "bf16_d64_bs16_g2": synth.Workload("bf16_d64_bs16_g2", 11, 8, 4, 64, 16, "bf16",
                                        ("uniform", 1, 2000), seed=35),
+    "bf16_d128_bs32_g2": synth.Workload("bf16_d128_bs32_g2", 5, 8, 4, 128, 32, "bf16",
+                                        ("uniform", 1, 700), num_blocks=120, seed=36),
+    "bf16_d64_bs32_g4": synth.Workload("bf16_d64_bs32_g4", 6, 16, 4, 64, 32, "bf16",
+                                       ("uniform", 1, 900), num_blocks=200, seed=37),
 }
 
 
@@ -145,6 +149,34 @@ def test_decode_matches_oracle(name):
     G.assert_close(out, ref, w.dtype, name)
 
 
+@pytest.mark.parametrize("name", ["mqa_large", "bf16_d64_bs32_g8", "bf16_d128_bs16_g16"])
+def test_vector_alu_kernel_matches_oracle(name, monkeypatch):
+    """The vector-ALU kernel on shapes the matrix-core kernel takes by default."""
+    monkeypatch.setenv("PAGEDATTN_DECODE_KERNEL", "valu")
+    inp = inputs_for(name)
+    w = inp["workload"]
+    say("write+decode (vector ALU kernel)", name)
+    d = G.upload(inp)
+    out = G.host_f64(gpu_step(d, w.partition_size))
+    ref, _ = oracle_step(inp)
+    G.assert_close(out, ref, w.dtype, name)
+
+
+@pytest.mark.parametrize("name", ["qwen3_0p6b", "bf16_d128_bs16_g16", "bf16_d64_bs32_g8"])
+@pytest.mark.parametrize("factor", [4.0, 16.0])
+def test_large_scores_match_oracle(name, factor):
+    """Scores several times wider than 1/sqrt(D) gives: the running maximum
+    moves often, in every tile, and the kept maximum is rescaled many times."""
+    inp = dict(inputs_for(name))
+    w = inp["workload"]
+    inp["scale"] = np.float32(inp["scale"] * factor)
+    say("decode scale x", factor, name)
+    d = G.upload(inp)
+    out = G.host_f64(gpu_step(d, w.partition_size))
+    ref, _ = oracle_step(inp)
+    G.assert_close(out, ref, w.dtype, f"{name} scale x{factor}")
+
+
 def test_decode_long_split_k_sampled():
     """32,768-token sequences, 512-token partitions (64 per sequence), merged
     in the same launch; the oracle checks every head of three sequences."""
@@ -181,7 +213,8 @@ def test_max_context_everywhere():
 
 
 @pytest.mark.parametrize("name", ["tiny_f32", "qwen3_0p6b", "bf16_d64_bs32_g8",
-                                  "f32_d128_bs32_g4", "mqa_large"])
+                                  "f32_d128_bs32_g4", "mqa_large", "bf16_d128_bs32_g2",
+                                  "bf16_d64_bs32_g4"])
 def test_single_token_exact(name):
     """P3 on the GPU: one cached token -> out is exactly that V row."""
     w = EXTRA.get(name) or synth.WORKLOADS[name]
@@ -197,12 +230,20 @@ def test_single_token_exact(name):
         assert np.array_equal(out[b], expect), b
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "gqa4_bf16"])
+ONEHOT = {
+    "gqa4_bf16": synth.Workload("gqa4_bf16", 6, 8, 2, 64, 16, "bf16", ("uniform", 1, 100),
+                                num_blocks=48, seed=21),
+    "gqa8_bf16": synth.Workload("gqa8_bf16", 4, 16, 2, 128, 32, "bf16", ("uniform", 1, 100),
+                                num_blocks=24, seed=22),
+    "mqa16_bf16": synth.Workload("mqa16_bf16", 5, 16, 1, 64, 16, "bf16", ("uniform", 1, 120),
+                                 num_blocks=48, seed=23),
+}
+
+
+@pytest.mark.parametrize("name", ["tiny_f32"] + list(ONEHOT))
 def test_onehot_exact(name):
     """P4 on the GPU: scale 1e5 -> out is exactly V of the top-scoring row."""
-    w = (synth.WORKLOADS["tiny_f32"] if name == "tiny_f32" else
-         synth.Workload("gqa4_bf16", 6, 8, 2, 32 * 2, 16, "bf16", ("uniform", 1, 100),
-                        num_blocks=48, seed=21))
+    w = synth.WORKLOADS["tiny_f32"] if name == "tiny_f32" else ONEHOT[name]
     inp, (k, v), best = P.onehot_inputs(w)
     say("decode one-hot", name)
     d = G.upload(inp)
@@ -247,7 +288,8 @@ def test_mqa_equals_replicated_mha():
     G.assert_close(mha, ref, "bf16", "replicated mha")
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "qwen3_0p6b", "bf16_d64_bs32_g8"])
+@pytest.mark.parametrize("name", ["tiny_f32", "qwen3_0p6b", "bf16_d64_bs32_g8",
+                                  "bf16_d128_bs32_g2", "bf16_d64_bs32_g4"])
 def test_nan_poison_bit_identical(name):
     """P13 on the GPU: NaN in unread slots and poison-padded tables change no bit."""
     w = EXTRA.get(name) or synth.WORKLOADS[name]
