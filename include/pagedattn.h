@@ -98,7 +98,7 @@ pa_status pa_reshape_and_cache(const void* key, const void* value,
 /*
  * The partition size (tokens) pa_paged_attention_decode will use for these
  * sizes: `requested` itself if it is a positive multiple of block_size no
- * larger than 64 * block_size; for `requested` 0 the library's own choice
+ * larger than 128 * block_size; for `requested` 0 the library's own choice
  * (1024 tokens at head_dim 128, 512 at head_dim 64 -- the fastest measured
  * on MI355X for the decode workloads); -1 if `requested` is invalid.
  */

@@ -389,11 +389,17 @@ __device__ __forceinline__ void reset_counter(int32_t* counter) {
 }
 
 // Where a partition workgroup stands: its sequence, kv-head group and
-// partition, the sequence's context length, this lane's block-table entry
-// (lane j holds the partition's block j), and how many blocks it streams.
+// partition, the sequence's context length, this lane's block-table entries
+// (lane l holds the partition's blocks l and 64 + l), and how many blocks it
+// streams.
 struct PartitionWork {
-  int b, gg, part, ctx, blk0, my_blk, nparts, nblk_run;
+  int b, gg, part, ctx, blk0, nparts, nblk_run;
+  int ent[2];
   bool poisoned;
+  // Physical id of the partition's block j (j wave-uniform, below 128).
+  __device__ __forceinline__ int block(int j) const {
+    return __builtin_amdgcn_readlane(j < 64 ? ent[0] : ent[1], j & 63);
+  }
 };
 
 // Start of a partition workgroup (grid x = (kv-head group, sequence), y =
@@ -415,7 +421,11 @@ __device__ __forceinline__ bool partition_prologue(const DecodeArgs& a, int lane
   w.ctx = a.context_lens[w.b];
   w.blk0 = w.part * a.part_blocks;
   const int32_t* trow = a.block_tables + (size_t)w.b * a.max_blocks + w.blk0;
-  w.my_blk = (lane < a.part_blocks && w.blk0 + lane < a.max_blocks) ? trow[lane] : 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = 64 * h + lane;
+    w.ent[h] = (e < a.part_blocks && w.blk0 + e < a.max_blocks) ? trow[e] : 0;
+  }
   load_q(w.b, w.gg);
 
   const int part_tokens = a.part_blocks * BS;
@@ -431,7 +441,10 @@ __device__ __forceinline__ bool partition_prologue(const DecodeArgs& a, int lane
   }
   const int nblk_seq = (w.ctx + BS - 1) / BS;
   const int nblk = min(a.part_blocks, nblk_seq - w.blk0);
-  const bool bad_here = lane < nblk && (w.my_blk < 0 || w.my_blk >= a.num_blocks);
+  bool bad_here = false;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    bad_here = bad_here || (64 * h + lane < nblk && (w.ent[h] < 0 || w.ent[h] >= a.num_blocks));
   w.poisoned = __ballot(bad_here) != 0;  // same answer in every wave
   w.nblk_run = w.poisoned ? 0 : nblk;
   return true;

@@ -119,6 +119,6 @@ inline bool aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
-constexpr int kMaxPartitionBlocks = 64;  // one table entry per lane of a wave
+constexpr int kMaxPartitionBlocks = 128;  // two table entries per lane of a wave
 
 }  // namespace pa

@@ -278,7 +278,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   const char* kbase = static_cast<const char*>(a.k_cache);
   const char* vbase = static_cast<const char*>(a.v_cache);
   auto fetch = [&](int jb, uint4 (&kr)[NI], uint4 (&vr)[NI]) {
-    const size_t boff = (size_t)__builtin_amdgcn_readlane(w.my_blk, jb) * blk_bytes;
+    const size_t boff = (size_t)w.block(jb) * blk_bytes;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(kbase + boff), 0, blk_bytes, kBufferRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(

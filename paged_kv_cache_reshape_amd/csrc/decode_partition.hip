@@ -4,8 +4,8 @@
 //   * a workgroup takes hpw consecutive kv heads (their rows are neighbours in
 //     every token) and all G query heads of each; every K/V byte is fetched
 //     from HBM once per (sequence, kv head);
-//   * the partition's block-table entries are read with one vector load (lane
-//     j holds entry j) and broadcast with readlane;
+//   * the partition's block-table entries are read with two vector loads
+//     (lane l holds entries l and 64 + l) and broadcast with readlane;
 //   * a sequence longer than one partition leaves one partial state per
 //     partition; the last workgroup of that (sequence, head group) to arrive
 //     merges them in the same launch (the last-block pattern of the LLAISYS
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
       }))
     return;
   const int g = w.gg * hpw + hw;
-  const int ctx = w.ctx, blk0 = w.blk0, my_blk = w.my_blk;
+  const int ctx = w.ctx, blk0 = w.blk0;
 
   st.reset();
   const size_t tok_stride = (size_t)Hkv * D;
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
   const S* kbase = static_cast<const S*>(a.k_cache) + (size_t)g * D + lane_off;
   const S* vbase = static_cast<const S*>(a.v_cache) + (size_t)g * D + lane_off;
   auto fetch = [&](int j, uint4 (&kr)[NI], uint4 (&vr)[NI]) {
-    const size_t off = (size_t)__builtin_amdgcn_readlane(my_blk, j) * blk_stride;
+    const size_t off = (size_t)w.block(j) * blk_stride;
     Row::fetch(kbase + off, vbase + off, tok_stride, kr, vr);
   };
   auto consume = [&](int j, bool live, const uint4 (&kr)[NI], const uint4 (&vr)[NI]) {

@@ -67,7 +67,7 @@ def _decode(lib, **kw):
     (dict(D=96), UNSUPPORTED),
     (dict(bs=8), UNSUPPORTED),
     (dict(ps=24), INVALID),                 # not a multiple of block_size
-    (dict(ps=16 * 65), INVALID),            # more than 64 blocks
+    (dict(ps=16 * 129), INVALID),           # more than 128 blocks
     (dict(Hkv=0), INVALID),
     (dict(nb=0), INVALID),
     (dict(B=-1), INVALID),
@@ -108,7 +108,8 @@ def test_partition_size_rule(lib):
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 512) == 512
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 500) == -1
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 64) == 1024
-    assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 65) == -1
+    assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 128) == 2048
+    assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 129) == -1
     # left to the library: 1024 tokens at head_dim 128, 512 at head_dim 64
     assert pa.decode_partition_size(32, 16, 8, 128, 128, 16, 0) == 1024
     assert pa.decode_partition_size(256, 32, 32, 128, 32, 32, 0) == 1024

@@ -190,7 +190,7 @@ def test_decode_long_split_k_sampled():
     G.assert_close(out[seqs], ref, w.dtype, "long_splitk")
 
 
-@pytest.mark.parametrize("ps", [16, 64, 256, 1024])
+@pytest.mark.parametrize("ps", [16, 64, 256, 1024, 1040, 2048])
 def test_partition_sizes_agree(ps):
     inp = inputs_for("qwen3_0p6b")
     say("decode qwen3 partition", ps)
