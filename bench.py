@@ -14,8 +14,11 @@ Prints one JSON line.  ``value`` is the step's algorithmic bytes (KV rows
 read, q read, output written, block-table entries, the write's rows) divided by
 the step time.  ``roofline`` is for the decode kernel alone: algorithmic bytes
 per launch over its mean launch time, from HIP events on the stream it runs on
-around K back-to-back launches.  ``cpu_baseline`` times the float64 CPU oracle
-on a bounded sample of the same batch.
+around K back-to-back launches.  ``graph_us_per_step`` is the same step
+replayed from a HIP graph.  ``prior_art`` times the pages' earlier design on
+the same GPU (gather the pages into dense tensors, then ordinary attention, in
+PyTorch).  ``cpu_baseline`` times the float64 CPU oracle on a bounded sample
+of the same batch.
 """
 from __future__ import annotations
 
@@ -78,6 +81,42 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+def decode_kernel_name(w) -> str:
+    """The decode kernel the library runs for this workload: the matrix-core
+    kernel for bfloat16 with 8, 16 or 32 query heads per kv head, the
+    vector-ALU kernel otherwise."""
+    g = w.num_q_heads // w.num_kv_heads
+    return "decode_mfma_kernel" if w.dtype == "bf16" and g in (8, 16, 32) \
+        else "decode_partition_kernel"
+
+
+def gather_then_attention(q, k_cache, v_cache, block_tables, context_lens, scale):
+    """The pages' prior art on the same GPU, in PyTorch: gather every
+    sequence's pages into dense, padded tensors, then ordinary masked
+    attention (barellm README, feature list: pages gathered into dense tensors
+    for SDPA; MinivLLM article, "What the Two Benchmark Scripts Compare": the
+    vectorised PyTorch decode with batch gathering and masking).  The gather
+    moves bf16 rows; the attention runs in float32 with contiguous matmul
+    operands.  Returns (out [B, Hq, D] in q's dtype, the dense K and V)."""
+    import torch
+    B, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    g = hq // hkv
+    idx = block_tables.clamp(min=0).long()
+    L = idx.shape[1] * bs
+    k = k_cache[idx].reshape(B, L, hkv, d)          # dense gather, bf16
+    v = v_cache[idx].reshape(B, L, hkv, d)
+    kt = k.permute(0, 2, 3, 1).float().contiguous()  # [B, Hkv, D, L]
+    vf = v.permute(0, 2, 1, 3).float().contiguous()  # [B, Hkv, L, D]
+    qf = q.float().reshape(B, hkv, g, d).contiguous()
+    s = torch.matmul(qf, kt) * scale                 # [B, Hkv, G, L]
+    live = torch.arange(L, device=q.device)[None, :] < context_lens[:, None].long()
+    s = s.masked_fill(~live[:, None, None, :], float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    out = torch.matmul(p, vf).reshape(B, hq, d)
+    return out.to(q.dtype), (k, v)
+
+
 def cpu_baseline(inp: dict, budget_s: float) -> dict:
     """Time the float64 oracle's write + decode on a bounded sample."""
     import oracle
@@ -124,6 +163,8 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for 1.25 GiB")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prior-art", action="store_true",
+                    help="skip timing the gather-then-attention PyTorch baseline")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -206,6 +247,42 @@ def main() -> int:
     k_mean_s = timed(decode, args.steps, args.warmup + args.steps) / 1e3
     w_mean_s = timed(write, args.steps, args.warmup) / 1e3
 
+    # The same steps replayed from a HIP graph (one graph holds one step per
+    # pool copy); buffers were all allocated above, so capture allocates nothing.
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for i in range(R):
+            step(i)
+    reps = max(1, args.steps // R)
+    graph.replay()
+    torch.cuda.synchronize()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_us = g0.elapsed_time(g1) * 1e3 / (reps * R)
+    del graph
+
+    prior = None
+    if not args.no_prior_art:
+        n_pa = 20
+        for i in range(3):
+            gather_then_attention(q, kcs[i % R], vcs[i % R], tables, lens, scale)
+        pa_ms = timed(lambda i: gather_then_attention(q, kcs[i % R], vcs[i % R], tables,
+                                                      lens, scale), n_pa, 0)
+        idx = tables.clamp(min=0).long()
+        ga_ms = timed(lambda i: (kcs[i % R][idx], vcs[i % R][idx]), n_pa, 0)
+        prior = {
+            "kind": "PyTorch: gather pages to dense padded bf16, masked attention in fp32",
+            "us_per_decode": round(pa_ms * 1e3, 3),
+            "dense_gather_us": round(ga_ms * 1e3, 3),
+            "decode_speedup": round(pa_ms / (k_mean_s * 1e3), 2),
+        }
+
     achieved = nbytes["decode"] / k_mean_s / 1e9
     traffic = None
     rec = traffic_record()
@@ -237,6 +314,7 @@ def main() -> int:
         "decode_us_mean": round(k_mean_s * 1e6, 3),
         "write_us_mean": round(w_mean_s * 1e6, 3),
         "decode_kv_gbs": round(nbytes["kv"] / k_mean_s / 1e9, 3),
+        "graph_us_per_step": round(graph_us, 3),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 3),
@@ -244,10 +322,12 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_partition_kernel",
+            "kernel": decode_kernel_name(w),
             "bytes_per_launch": nbytes["decode"],
         },
     }
+    if prior is not None:
+        res["prior_art"] = prior
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(res), flush=True)

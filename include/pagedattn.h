@@ -96,11 +96,35 @@ pa_status pa_reshape_and_cache(const void* key, const void* value,
                                void* stream);
 
 /*
+ * Block copy for copy-on-write of shared blocks.  Sequences that share a
+ * prompt prefix may name the same physical block in their block tables
+ * (block sharing and prefix caching: MinivLLM article, "Running It" section;
+ * nano-vllm overview, "Kernmodul: Sequence"); before a sequence writes a new
+ * token into a block it shares, the caller gives it a private copy.
+ *
+ * For each i < num_pairs with src = block_pairs[2i], dst = block_pairs[2i+1],
+ * both in [0, num_blocks): block dst of k_cache and of v_cache becomes a
+ * bit-exact copy of block src.  Pairs naming a block outside the pool are
+ * skipped.  A block that is the destination of two pairs, or the destination
+ * of one and the source of another, ends in an unspecified state.
+ *
+ *   k_cache, v_cache [num_blocks, block_size, num_kv_heads, head_dim] (read/written)
+ *   block_pairs      [num_pairs, 2] int64, device memory            (read)
+ *
+ * num_pairs == 0 is a valid no-op.  Asynchronous on `stream`.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t num_blocks, int32_t block_size, pa_dtype dtype,
+                         void* stream);
+
+/*
  * The partition size (tokens) pa_paged_attention_decode will use for these
  * sizes: `requested` itself if it is a positive multiple of block_size no
  * larger than 128 * block_size; for `requested` 0 the library's own choice
- * (1024 tokens at head_dim 128, 512 at head_dim 64 -- the fastest measured
- * on MI355X for the decode workloads); -1 if `requested` is invalid.
+ * (512 tokens at head_dim 64; at head_dim 128, 1024 tokens, or 2048 when
+ * max_blocks_per_seq * block_size exceeds 4096 -- the fastest measured on
+ * MI355X for the decode workloads); -1 if `requested` is invalid.
  */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim,

@@ -12,6 +12,7 @@ See ``oracle.paged_attention`` for the definitions and their citations.
 from .paged_attention import (  # noqa: F401
     widen,
     reshape_and_cache,
+    copy_blocks,
     gather_kv,
     decode,
     decode_one,

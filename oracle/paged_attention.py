@@ -78,6 +78,28 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping):
     return k_out, v_out
 
 
+def copy_blocks(k_cache, v_cache, block_pairs):
+    """Copy-on-write of shared blocks.  Returns new (k_cache, v_cache).
+
+    Sequences with a common prompt prefix may name the same physical blocks
+    in their tables (block sharing: MinivLLM article, "Running It" section;
+    prefix caching: nano-vllm overview, "Kernmodul: Sequence").  Reading
+    taken where the pages are silent: before one of them writes into a shared
+    block it gets a private copy.  For each (src, dst) row of ``block_pairs``,
+    in order, with both ids inside the pool: block dst of both caches becomes
+    a copy of block src.  Rows naming a block outside the pool are skipped.
+    """
+    k_out = np.array(k_cache, copy=True)
+    v_out = np.array(v_cache, copy=True)
+    num_blocks = k_cache.shape[0]
+    for src, dst in np.asarray(block_pairs, dtype=np.int64).reshape(-1, 2):
+        if not (0 <= src < num_blocks and 0 <= dst < num_blocks):
+            continue
+        k_out[dst] = k_out[src]
+        v_out[dst] = v_out[src]
+    return k_out, v_out
+
+
 def gather_kv(cache, block_tables, context_lens):
     """Exact gather of each sequence's cached rows into a dense tensor.
 

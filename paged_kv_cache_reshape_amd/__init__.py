@@ -75,6 +75,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.pa_paged_attention_decode.argtypes = [
             vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
             vp, sz, vp, i64, i32, vp]
+        lib.pa_copy_blocks.restype = i32
+        lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
         lib.pa_debug_gather_kv.restype = i32
         lib.pa_debug_gather_kv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                            i32, i32, i32, vp]
@@ -134,6 +136,27 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Ten
             key.data_ptr(), value.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             slot_mapping.data_ptr(), key.shape[0], hkv, d, nb, bs, dt, _stream(dev))
     _check(st, "pa_reshape_and_cache")
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
+                block_pairs: torch.Tensor) -> None:
+    """Copy-on-write of shared blocks: for each row (src, dst) of the int64
+    ``[n, 2]`` device tensor ``block_pairs``, block dst of both caches becomes
+    a copy of block src."""
+    lib = load_library()
+    dev = _same_device(k_cache, v_cache, block_pairs)
+    _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape,
+          "caches must be [num_blocks, block_size, Hkv, D] and alike")
+    _need(block_pairs.dtype == torch.int64 and block_pairs.dim() == 2
+          and block_pairs.shape[1] == 2 and block_pairs.is_contiguous(),
+          "block_pairs must be a contiguous int64 [n, 2] tensor")
+    nb, bs, hkv, d = k_cache.shape
+    dt = _dtype_code(k_cache)
+    _need(v_cache.dtype == k_cache.dtype, "dtype mismatch")
+    with torch.cuda.device(dev):
+        st = lib.pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), block_pairs.data_ptr(),
+                                block_pairs.shape[0], hkv, d, nb, bs, dt, _stream(dev))
+    _check(st, "pa_copy_blocks")
 
 
 def decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,

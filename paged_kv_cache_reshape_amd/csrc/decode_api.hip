@@ -39,12 +39,18 @@ int heads_per_workgroup(int Hkv, int G, int D) {
   return 1;
 }
 
-// Library choice of partition length.  Measured on MI355X over the decode
+// Library choice of partition length, from the head size and the longest
+// context the block table can describe.  Measured on MI355X over the decode
 // workloads (Qwen3-, Llama-3.2-shaped, long-context, large-batch MHA/MQA):
-// long partitions win -- few workgroups streaming about 1 MB each keep every
-// compute unit's queue of outstanding loads full, and fewer sequences need a
-// merge -- except at head_dim 64, where 512 tokens is better.
-int auto_partition_tokens(int D) { return D == 128 ? 1024 : 512; }
+// long partitions win -- a compute unit streams at most about 40 GB/s, so
+// what counts is that the longest partitions are few and large ones carry no
+// merge -- except at head_dim 64, where 512 tokens is better; tables of more
+// than 4096 tokens (the 32K-token batch: 191 us at 2048, 200 us at 1024)
+// take 2048.
+int auto_partition_tokens(int D, int max_tokens) {
+  if (D != 128) return 512;
+  return max_tokens > 4096 ? 2048 : 1024;
+}
 
 // The matrix-core kernel where it applies.  PAGEDATTN_DECODE_KERNEL=valu
 // forces the vector-ALU kernel (tests compare the two).
@@ -69,7 +75,7 @@ bool make_plan(int B, int Hq, int Hkv, int D, int max_blocks, int bs, int reques
   const int G = Hq / Hkv;
   if (!group_supported(G)) return false;
   p->hpw = heads_per_workgroup(Hkv, G, D);
-  const int tokens = requested == 0 ? auto_partition_tokens(D) : requested;
+  const int tokens = requested == 0 ? auto_partition_tokens(D, max_blocks * bs) : requested;
   if (tokens < 0 || tokens % bs != 0) return false;
   const int pb = tokens / bs;
   if (pb < 1 || pb > kMaxPartitionBlocks) return false;

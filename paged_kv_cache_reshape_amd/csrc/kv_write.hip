@@ -1,4 +1,5 @@
-// Paged KV write (reshape_and_cache) and the dense debug gather, gfx950.
+// Paged KV write (reshape_and_cache), block copy (copy-on-write of shared
+// blocks) and the dense debug gather, gfx950.
 //
 // The write is the cache's logical-to-physical write (barellm README,
 // paged-cache component list): each new token's K and V rows go to the slot
@@ -27,6 +28,27 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
   const uint4 vv = value[i];
   k_cache[slot * row_chunks + c] = kv;
   v_cache[slot * row_chunks + c] = vv;
+}
+
+// Block dst of both caches becomes a copy of block src, for each (src, dst)
+// pair; grid x = pair, grid y = slices of the block.  A block shared by
+// several sequences (their tables name the same physical block for a common
+// prefix: MinivLLM article, "Running It" section; nano-vllm overview,
+// prefix caching in "Kernmodul: Sequence") is copied before one of them
+// writes into it.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    uint4* k_cache, uint4* v_cache, const int64_t* __restrict__ block_pairs,
+    int64_t blk_chunks, int64_t num_blocks) {
+  const int64_t src = block_pairs[2 * (int64_t)blockIdx.x];
+  const int64_t dst = block_pairs[2 * (int64_t)blockIdx.x + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const int64_t step = (int64_t)gridDim.y * blockDim.x;
+  for (int64_t c = (int64_t)blockIdx.y * blockDim.x + threadIdx.x; c < blk_chunks; c += step) {
+    const uint4 kv = k_cache[src * blk_chunks + c];
+    const uint4 vv = v_cache[src * blk_chunks + c];
+    k_cache[dst * blk_chunks + c] = kv;
+    v_cache[dst * blk_chunks + c] = vv;
+  }
 }
 
 // dense[b, t] = cache[table[b, t / bs], t % bs] for t < ctx_b, zero bytes
@@ -126,6 +148,42 @@ extern "C" pa_status pa_reshape_and_cache(const void* key, const void* value,
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) {
     set_error("reshape_and_cache launch failed: %s", hipGetErrorString(err));
+    return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+extern "C" pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
+                                    int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t num_blocks, int32_t block_size, pa_dtype dtype,
+                                    void* stream) {
+  clear_error();
+  pa_status st = check_cache_args(num_kv_heads, head_dim, num_blocks, block_size, dtype);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) {
+    set_error("num_pairs=%d is negative", num_pairs);
+    return PA_ERR_INVALID_ARGUMENT;
+  }
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_pairs) {
+    set_error("a tensor pointer is NULL");
+    return PA_ERR_INVALID_ARGUMENT;
+  }
+  if (!aligned16(k_cache) || !aligned16(v_cache)) {
+    set_error("k_cache and v_cache must be 16-byte aligned");
+    return PA_ERR_INVALID_ARGUMENT;
+  }
+  const int64_t blk_chunks =
+      (int64_t)block_size * num_kv_heads * head_dim * dtype_bytes(dtype) / 16;
+  // Enough slices that one block's chunks are one or two passes of 256 lanes.
+  const unsigned slices = (unsigned)((blk_chunks + 511) / 512);
+  copy_blocks_kernel<<<dim3((unsigned)num_pairs, slices), 256, 0,
+                       static_cast<hipStream_t>(stream)>>>(
+      static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), block_pairs, blk_chunks,
+      num_blocks);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) {
+    set_error("copy_blocks launch failed: %s", hipGetErrorString(err));
     return PA_ERR_HIP;
   }
   return PA_OK;

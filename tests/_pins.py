@@ -405,3 +405,71 @@ def pin_empty_sequence(dec, rac, w):
         if np.max(np.abs(out[b] - ref)) > 1e-12:
             return False, f"seq {b} wrong"
     return True, ""
+
+
+# ---------------------------------------------------------------- shared blocks
+def pin_copy_blocks(copy, inp, pairs):
+    """P15: after the copy, the rows of each destination block equal the rows
+    its source block held, bit for bit; blocks that are no destination keep
+    their bits; pairs naming a block outside the pool change nothing.
+
+    Expected values come from the flat-slot view ([num_blocks * bs, ...]):
+    block n is flat rows n*bs .. n*bs+bs-1 (row-major layout).  ``pairs``
+    must not chain (no block is both a source and a destination).
+    """
+    kc, vc = inp["k_cache"], inp["v_cache"]
+    nb, bs = kc.shape[:2]
+    k2, v2 = copy(kc, vc, pairs)
+    for old, new in ((kc, k2), (vc, v2)):
+        flat_old = old.reshape((nb * bs,) + old.shape[2:])
+        flat_new = new.reshape((nb * bs,) + new.shape[2:])
+        dest = np.zeros(nb * bs, dtype=bool)
+        for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+            if not (0 <= src < nb and 0 <= dst < nb):
+                continue
+            rows = slice(dst * bs, dst * bs + bs)
+            dest[rows] = True
+            if flat_new[rows].tobytes() != flat_old[src * bs:src * bs + bs].tobytes():
+                return False, f"block {dst} is not a copy of block {src}"
+        if flat_new[~dest].tobytes() != flat_old[~dest].tobytes():
+            return False, "a block that is no destination changed"
+    return True, ""
+
+
+def pin_shared_prefix(dec, rac, w, members=(0, 1, 2), prefix_blocks=2):
+    """P16: sequences whose tables name the same physical blocks for a common
+    prefix decode exactly as if each held its own copy of those blocks
+    (paging only changes where rows live).  The private copies are made by
+    gathering the shared rows chunk by chunk and storing them in fresh
+    blocks, independently of the oracle's block copy."""
+    inp = synth.make_inputs(w)
+    k, v = written(inp, rac)
+    tables = inp["block_tables"].copy()
+    ctx = inp["context_lens"]
+    bs = w.block_size
+    lead = members[0]
+    for b in members:
+        if int(ctx[b]) <= prefix_blocks * bs:
+            return False, f"member {b} too short for the shared prefix"
+    shared = tables.copy()
+    for b in members[1:]:
+        shared[b, :prefix_blocks] = tables[lead, :prefix_blocks]
+    out_shared = _dec(dec, inp, k, v, block_tables=shared)
+    # Private copies: append one fresh block per (member, prefix block).
+    extra = len(members[1:]) * prefix_blocks
+    k2 = np.concatenate([k, np.zeros((extra,) + k.shape[1:], k.dtype)])
+    v2 = np.concatenate([v, np.zeros((extra,) + v.shape[1:], v.dtype)])
+    private = shared.copy()
+    nxt = k.shape[0]
+    for b in members[1:]:
+        rows_k = dense_from_chunks(k, tables[lead], prefix_blocks * bs)
+        rows_v = dense_from_chunks(v, tables[lead], prefix_blocks * bs)
+        for j in range(prefix_blocks):
+            k2[nxt] = rows_k[j * bs:(j + 1) * bs]
+            v2[nxt] = rows_v[j * bs:(j + 1) * bs]
+            private[b, j] = nxt
+            nxt += 1
+    out_private = _dec(dec, inp, k2, v2, block_tables=private)
+    if not np.array_equal(out_shared, out_private):
+        return False, "aliased prefix blocks change the result"
+    return True, ""

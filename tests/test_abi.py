@@ -96,6 +96,16 @@ def test_write_argument_checks(lib):
     assert f(16, 24, 16, 16, 16, 4, 2, 64, 32, 16, 0, None) == INVALID  # misaligned
 
 
+def test_copy_blocks_argument_checks(lib):
+    f = lib.pa_copy_blocks
+    assert f(16, 16, 16, 0, 2, 64, 32, 16, 0, None) == OK          # no pairs
+    assert f(16, 16, 16, -1, 2, 64, 32, 16, 0, None) == INVALID
+    assert f(16, 16, None, 3, 2, 64, 32, 16, 0, None) == INVALID
+    assert f(16, 24, 16, 3, 2, 64, 32, 16, 0, None) == INVALID     # misaligned
+    assert f(16, 16, 16, 3, 2, 64, 32, 8, 0, None) == UNSUPPORTED
+    assert f(16, 16, 16, 3, 0, 64, 32, 16, 0, None) == INVALID
+
+
 def test_gather_argument_checks(lib):
     f = lib.pa_debug_gather_kv
     assert f(16, 16, 16, 16, 16, 16, 0, 2, 64, 32, 16, 4, 0, None) == OK
@@ -112,6 +122,9 @@ def test_partition_size_rule(lib):
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 129) == -1
     # left to the library: 1024 tokens at head_dim 128, 512 at head_dim 64
     assert pa.decode_partition_size(32, 16, 8, 128, 128, 16, 0) == 1024
+    assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 0) == 2048
+    assert pa.decode_partition_size(8, 32, 8, 128, 256, 16, 0) == 1024
+    assert pa.decode_partition_size(8, 32, 8, 128, 257, 16, 0) == 2048
     assert pa.decode_partition_size(256, 32, 32, 128, 32, 32, 0) == 1024
     assert pa.decode_partition_size(64, 32, 8, 64, 256, 16, 0) == 512
     assert pa.decode_partition_size(4, 4, 2, 64, 4, 16, 0) == 512
@@ -164,3 +177,4 @@ def test_ctypes_signatures_match_header(lib):
     assert len(lib.pa_paged_attention_decode.argtypes) == 21
     assert len(lib.pa_reshape_and_cache.argtypes) == 12
     assert len(lib.pa_debug_gather_kv.argtypes) == 14
+    assert len(lib.pa_copy_blocks.argtypes) == 10

@@ -386,3 +386,125 @@ def test_one_counter_array_serves_every_geometry():
         ref, _ = oracle_step(inp)
         G.assert_close(G.host_f64(out), ref, w.dtype, f"{name} ps={ps}")
         assert int(cnt.abs().sum()) == 0
+
+
+# ------------------------------------------------------------------ shared blocks
+@pytest.mark.parametrize("name", ["tiny_f32", "qwen3_0p6b", "bf16_d128_bs32_g2"])
+def test_copy_blocks_bit_exact(name):
+    """P15 on the GPU: block copies (pairs outside the pool skipped)."""
+    inp = inputs_for(name)
+    nb = inp["num_blocks"]
+    pairs = np.array([[1, nb - 1], [3, 0], [-1, 2], [2, nb], [5, nb - 2], [7, 9]],
+                     dtype=np.int64)
+    say("copy_blocks", name)
+    d = G.upload(inp)
+    pa.copy_blocks(d["k_cache"], d["v_cache"], torch.from_numpy(pairs).cuda())
+    k_ref, v_ref = oracle.copy_blocks(inp["k_cache"], inp["v_cache"], pairs)
+    assert np.array_equal(G.host_storage(d["k_cache"]), k_ref)
+    assert np.array_equal(G.host_storage(d["v_cache"]), v_ref)
+
+
+def test_prefix_fork_copy_on_write():
+    """Sequences sharing prompt-prefix blocks: sequences 2 and 3 name sequence
+    0's first two (full) blocks in their tables; sequence 1 forks sequence 0's
+    whole 49-token history, whose last block is partly filled, so it gets a
+    private copy of that block before its own new token goes in.  Copy, write
+    and decode on the GPU against the oracle taking the same steps."""
+    w = synth.Workload("fork_bf16", 4, 8, 2, 128, 16, "bf16", ("uniform", 40, 60),
+                       num_blocks=64, seed=41)
+    ctx = np.array([50, 50, 45, 58], dtype=np.int32)
+    inp = dict(synth.make_inputs(w, context_lens=ctx))
+    bs = w.block_size
+    tables = inp["block_tables"].copy()
+    slots = inp["slot_mapping"].copy()
+    last = (int(ctx[0]) - 1) // bs               # block holding position 49
+    used = set(int(x) for x in tables[tables >= 0].ravel())
+    fresh = next(x for x in range(inp["num_blocks"]) if x not in used)
+    tables[1, :] = -1
+    tables[1, :last + 1] = tables[0, :last + 1]
+    tables[1, last] = fresh
+    slots[1] = fresh * bs + (int(ctx[1]) - 1) % bs
+    tables[2, :2] = tables[0, :2]
+    tables[3, :2] = tables[0, :2]
+    pairs = np.array([[tables[0, last], fresh]], dtype=np.int64)
+    inp.update(block_tables=tables, slot_mapping=slots)
+    say("prefix fork: copy, write, decode")
+    d = G.upload(inp)
+    pa.copy_blocks(d["k_cache"], d["v_cache"], torch.from_numpy(pairs).cuda())
+    out = G.host_f64(gpu_step(d))
+    k_ref, v_ref = oracle.copy_blocks(inp["k_cache"], inp["v_cache"], pairs)
+    k_ref, v_ref = oracle.reshape_and_cache(inp["key"], inp["value"], k_ref, v_ref, slots)
+    ref = oracle.decode(inp["q"], k_ref, v_ref, tables, ctx, inp["scale"], "bf16")
+    assert np.array_equal(G.host_storage(d["k_cache"]), k_ref)
+    assert np.array_equal(G.host_storage(d["v_cache"]), v_ref)
+    G.assert_close(out, ref, "bf16", "prefix fork")
+    # Sequence 1 saw sequence 0's history, not its new token.
+    assert not np.array_equal(out[0], out[1])
+
+
+# ------------------------------------------------------------------ graph capture
+@pytest.mark.parametrize("name", ["qwen3_0p6b", "mqa_large"])
+def test_graph_replays_match_eager(name):
+    """A step (KV write + decode) captured in a HIP graph: every replay, with
+    eager launches and host synchronisations between replays, gives the eager
+    result bit for bit.  The workspace and the arrival counters are allocated
+    before capture and passed in, so nothing is allocated or cleared inside
+    the graph (the kernels leave the counters at zero themselves)."""
+    inp = inputs_for(name)
+    w = inp["workload"]
+    say("graph capture", name)
+    d = G.upload(inp)
+    B, hq, hkv = w.num_seqs, w.num_q_heads, w.num_kv_heads
+    mb = d["block_tables"].shape[1]
+    ps = w.partition_size
+    ws = torch.empty(max(pa.decode_workspace_bytes(B, hq, hkv, w.head_dim, mb, w.block_size,
+                                                   ps), 256), dtype=torch.uint8, device="cuda")
+    cnt = torch.zeros(B * hkv, dtype=torch.int32, device="cuda")
+
+    def step(out):
+        pa.reshape_and_cache(d["key"], d["value"], d["k_cache"], d["v_cache"],
+                             d["slot_mapping"])
+        pa.paged_attention_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                  d["context_lens"], d["scale"], partition_size=ps, out=out,
+                                  workspace=ws, counters=cnt)
+
+    eager = torch.empty_like(d["q"])
+    step(eager)
+    torch.cuda.synchronize()
+    expect = G.host_storage(eager)
+    graphed = torch.full_like(d["q"], float("nan"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):       # warm-up on the capture stream
+        step(graphed)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(graphed)
+    scratch = torch.empty_like(d["q"])
+    for r in range(4):
+        graphed.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(G.host_storage(graphed), expect), f"replay {r}"
+        step(scratch)                    # eager work between replays
+        torch.cuda.synchronize()
+    assert int(cnt.abs().sum()) == 0
+
+
+# ------------------------------------------------------------------ prior art
+@pytest.mark.parametrize("name", ["qwen3_0p6b", "bf16_d64_bs32_g8"])
+def test_prior_art_baseline_matches_oracle(name):
+    """The gather-then-attention PyTorch baseline that bench.py times beside
+    the kernel computes the same decode (so the comparison is like for like)."""
+    import bench
+    inp = inputs_for(name)
+    w = inp["workload"]
+    say("prior-art baseline", name)
+    d = G.upload(inp)
+    pa.reshape_and_cache(d["key"], d["value"], d["k_cache"], d["v_cache"], d["slot_mapping"])
+    out, _ = bench.gather_then_attention(d["q"], d["k_cache"], d["v_cache"],
+                                         d["block_tables"], d["context_lens"], d["scale"])
+    ref, _ = oracle_step(inp)
+    G.assert_close(G.host_f64(out), ref, w.dtype, f"{name} baseline")

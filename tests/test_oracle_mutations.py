@@ -191,3 +191,25 @@ def test_gather_mutant_is_caught():
         return g
     ok, _ = P.pin_gather_chunks(gather_no_zero, synth.make_inputs(W_BF16))
     assert not ok
+
+
+@pytest.mark.parametrize("kind", ["k_only", "swapped", "no_bounds"])
+def test_copy_mutant_is_caught(kind):
+    def copy(k_cache, v_cache, block_pairs):
+        k_out, v_out = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+        nb = k_cache.shape[0]
+        for src, dst in np.asarray(block_pairs, dtype=np.int64).reshape(-1, 2):
+            if kind != "no_bounds" and not (0 <= src < nb and 0 <= dst < nb):
+                continue
+            if kind == "swapped":
+                src, dst = dst, src
+            k_out[dst % nb] = k_out[src % nb]
+            if kind != "k_only":
+                v_out[dst % nb] = v_out[src % nb]
+        return k_out, v_out
+    inp = synth.make_inputs(W_BF16)
+    nb = inp["num_blocks"]
+    pairs = np.array([[1, nb - 1], [3, 0], [-1, 2], [2, nb]], dtype=np.int64)
+    ok, _ = P.pin_copy_blocks(copy, inp, pairs)
+    assert not ok
+

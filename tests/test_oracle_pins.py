@@ -160,3 +160,28 @@ def test_merge_is_order_free():
     a = oracle.merge_partials(m, l, acc)
     b = oracle.merge_partials(m[:, :, perm], l[:, :, perm], acc[:, :, perm])
     assert np.max(np.abs(a - b)) <= 1e-13
+
+
+# ------------------------------------------------------------ shared blocks
+def _pairs(nb):
+    # Sources and destinations disjoint; two pairs name blocks outside the pool.
+    return np.array([[1, nb - 1], [3, 0], [-1, 2], [2, nb], [5, nb - 2]], dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_p15_copy_blocks(name):
+    inp = synth.make_inputs(SMALL[name])
+    _ok(P.pin_copy_blocks(oracle.copy_blocks, inp, _pairs(inp["num_blocks"])))
+
+
+@pytest.mark.parametrize("name,prefix_blocks", [("gqa4_bf16", 2), ("mha_f32", 1),
+                                                ("mqa_bf16_bs32", 1)])
+def test_p16_shared_prefix(name, prefix_blocks):
+    w = SMALL[name]
+    inp = synth.make_inputs(w)
+    # Members: the sequences long enough to hold the shared prefix and a token.
+    long_enough = inp["context_lens"] > prefix_blocks * w.block_size
+    members = tuple(int(b) for b in np.nonzero(long_enough)[0])
+    assert len(members) >= 2
+    _ok(P.pin_shared_prefix(oracle.decode, oracle.reshape_and_cache, w, members,
+                            prefix_blocks))
