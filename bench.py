@@ -40,7 +40,7 @@ import synth  # noqa: E402
 
 METRIC = "decode-attention KV GB/s and % of HBM peak; µs/step at B=32 Qwen3-0.6B shape"
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_reshape_amd", "csrc", f)
                for f in ("decode_partition.hip", "decode_mfma.hip", "attn_common.hpp",
                          "common.hpp", "decode_launch.hpp", "decode_api.hip")]
@@ -60,11 +60,16 @@ def algorithmic_bytes(inp: dict) -> dict:
                 step=kv + qo + tables + write)
 
 
-def traffic_record():
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"traffic_{workload}.json")
+
+
+def traffic_record(workload: str):
     """HBM bytes per decode launch from committed rocprofv3 counter runs, if
-    they were taken on the decode kernel as it is now (source hash matches)."""
+    they were taken on the decode kernels as they are now (source hash
+    matches)."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(traffic_file(workload)))
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256") != kernel_source_hash():
@@ -163,6 +168,8 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for 1.25 GiB")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the step replayed from a HIP graph")
     ap.add_argument("--no-prior-art", action="store_true",
                     help="skip timing the gather-then-attention PyTorch baseline")
     args = ap.parse_args()
@@ -249,23 +256,25 @@ def main() -> int:
 
     # The same steps replayed from a HIP graph (one graph holds one step per
     # pool copy); buffers were all allocated above, so capture allocates nothing.
-    graph = torch.cuda.CUDAGraph()
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph):
-        for i in range(R):
-            step(i)
-    reps = max(1, args.steps // R)
-    graph.replay()
-    torch.cuda.synchronize()
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
-    g0.record(stream)
-    for _ in range(reps):
+    graph_us = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            for i in range(R):
+                step(i)
+        reps = max(1, args.steps // R)
         graph.replay()
-    g1.record(stream)
-    torch.cuda.synchronize()
-    graph_us = g0.elapsed_time(g1) * 1e3 / (reps * R)
-    del graph
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_us = g0.elapsed_time(g1) * 1e3 / (reps * R)
+        del graph
 
     prior = None
     if not args.no_prior_art:
@@ -285,7 +294,7 @@ def main() -> int:
 
     achieved = nbytes["decode"] / k_mean_s / 1e9
     traffic = None
-    rec = traffic_record()
+    rec = traffic_record(w.name)
     if rec and rec.get("workload") == w.name and rec.get("partition_size") == part:
         traffic = rec.get("hbm_bytes_per_launch")
     res = {
@@ -314,7 +323,7 @@ def main() -> int:
         "decode_us_mean": round(k_mean_s * 1e6, 3),
         "write_us_mean": round(w_mean_s * 1e6, 3),
         "decode_kv_gbs": round(nbytes["kv"] / k_mean_s / 1e9, 3),
-        "graph_us_per_step": round(graph_us, 3),
+        "graph_us_per_step": None if graph_us is None else round(graph_us, 3),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 3),

@@ -5,7 +5,7 @@ Commands (run on the CSV files a GPU run wrote):
   python -m paged_kv_cache_reshape_amd.profiling trace KERNEL_STATS_CSV OUT_MD \\
       --command "<the rocprofv3 command that produced it>"
 
-  python -m paged_kv_cache_reshape_amd.profiling traffic FETCH_CSV WRITE_CSV OUT_JSON \\
+  python -m paged_kv_cache_reshape_amd.profiling traffic FETCH_CSV WRITE_CSV \\
       --workload qwen3_0p6b --partition-size 1024 --command "<...>"
 
 ``traffic`` scales the per-dispatch FETCH_SIZE and WRITE_SIZE of the decode
@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 
 
 def _kernel_key(name: str) -> str:
-    if "decode_partition_kernel" in name:
+    if "decode_partition_kernel" in name or "decode_mfma_kernel" in name:
         return "decode"
     if "kv_write_kernel" in name:
         return "kv_write"
@@ -64,8 +64,8 @@ def _per_dispatch(counter_csv: str, counter: str) -> dict:
     return {k: sum(v) / len(v) for k, v in agg.items()}
 
 
-def traffic_record(fetch_csv: str, write_csv: str, out_json: str, workload: str,
-                   partition_size: int, command: str) -> dict:
+def traffic_record(fetch_csv: str, write_csv: str, workload: str, partition_size: int,
+                   command: str) -> dict:
     import numpy as np
 
     import bench
@@ -84,10 +84,11 @@ def traffic_record(fetch_csv: str, write_csv: str, out_json: str, workload: str,
     read_b = fetch["decode"] * fetch_factor * 1024.0
     write_b = write["decode"] * write_factor * 1024.0
     inp_bytes = bench.algorithmic_bytes(synth.make_inputs(w))["decode"]
+    out_json = bench.traffic_file(workload)
     rec = {
         "workload": workload,
         "partition_size": partition_size,
-        "kernel": "decode_partition_kernel",
+        "kernel": bench.decode_kernel_name(w),
         "command": command,
         "fetch_size_kib_per_dispatch": round(fetch["decode"], 2),
         "write_size_kib_per_dispatch": round(write["decode"], 2),
@@ -106,7 +107,7 @@ def traffic_record(fetch_csv: str, write_csv: str, out_json: str, workload: str,
     json.dump(rec, open(out_json, "w"), indent=1)
     md = os.path.splitext(out_json)[0] + ".md"
     open(md, "w").write(
-        "# HBM traffic of the decode kernel\n\n"
+        f"# HBM traffic of {rec['kernel']}\n\n"
         f"Workload `{workload}`, partition size {partition_size}.\n\n"
         "Commands (one counter per run):\n\n```\n" + command + "\n```\n\n"
         "| | FETCH_SIZE (KiB/dispatch) | WRITE_SIZE (KiB/dispatch) |\n|---|---|---|\n"
@@ -129,7 +130,6 @@ def main(argv=None) -> int:
     f = sub.add_parser("traffic")
     f.add_argument("fetch_csv")
     f.add_argument("write_csv")
-    f.add_argument("out_json")
     f.add_argument("--workload", default="qwen3_0p6b")
     f.add_argument("--partition-size", type=int, required=True)
     f.add_argument("--command", required=True)
@@ -137,7 +137,7 @@ def main(argv=None) -> int:
     if a.cmd == "trace":
         trace_summary(a.stats_csv, a.out_md, a.command)
     else:
-        print(json.dumps(traffic_record(a.fetch_csv, a.write_csv, a.out_json, a.workload,
+        print(json.dumps(traffic_record(a.fetch_csv, a.write_csv, a.workload,
                                         a.partition_size, a.command), indent=1))
     return 0
 
