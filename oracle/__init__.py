@@ -16,6 +16,7 @@ from .paged_attention import (  # noqa: F401
     gather_kv,
     decode,
     decode_one,
+    prefill,
     decode_partials,
     merge_partials,
 )

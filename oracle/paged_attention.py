@@ -164,6 +164,43 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, dtype):
     return out
 
 
+def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, dtype):
+    """Paged prefill (and chunked-prefill) attention, causal, float64.
+
+    The step before decode on the pages' data flow: a prompt, or a chunk of
+    it after a cached prefix, is processed at once, each new token attending
+    to every cached position up to its own (MinivLLM article, "Engine
+    Layout": prefilling vs decoding; nano-vllm overview, "Prefill vs.
+    Decode").  Sequence b's new query rows are
+    ``q[query_start[b] : query_start[b+1]]``; with ``L = context_lens[b]`` and
+    ``n`` new rows, row i sits at position ``L - n + i`` and attends to the
+    cached positions ``0 .. L - n + i`` (its own row, written by the KV write,
+    included).  Returns out [T, Hq, D] float64; rows of a sequence with
+    ``n > L`` are NaN (there is no such position).
+    """
+    scale = np.float64(np.float32(scale))
+    qf = widen(q, dtype)
+    out = np.zeros(qf.shape, dtype=np.float64)
+    bs = k_cache.shape[1]
+    for b in range(len(context_lens)):
+        L = int(context_lens[b])
+        lo, hi = int(query_start[b]), int(query_start[b + 1])
+        n = hi - lo
+        if n <= 0:
+            continue
+        if n > L:
+            out[lo:hi] = np.nan
+            continue
+        pos = np.arange(L)
+        phys = block_tables[b, pos // bs].astype(np.int64)
+        K = widen(k_cache[phys, pos % bs], dtype)
+        V = widen(v_cache[phys, pos % bs], dtype)
+        for i in range(n):
+            p = L - n + i
+            out[lo + i] = decode_one(qf[lo + i], K[:p + 1], V[:p + 1], scale)
+    return out
+
+
 def decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale,
                     dtype, partition_size):
     """Per-partition softmax state, for the split-K merge identity.

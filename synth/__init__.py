@@ -41,6 +41,8 @@ __all__ = [
     "Workload",
     "WORKLOADS",
     "make_inputs",
+    "PREFILL_WORKLOADS",
+    "make_prefill_inputs",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
     "storage_np_dtype",
@@ -64,6 +66,11 @@ class Workload:
     max_blocks: int | None = None  # None: ceil(largest possible ctx / block_size)
     partition_size: int = 0  # 0: library chooses
     seed: int = 0
+    # Prefill only: new query tokens per sequence, the last ones of its
+    # context.  ("full",): the whole context (a prompt from scratch);
+    # ("uniform", lo, hi) / ("fixed", (n0, n1, ...)): a chunk after a cached
+    # prefix, clipped to the context length.
+    query: tuple | None = None
 
     @property
     def max_ctx(self) -> int:
@@ -254,4 +261,98 @@ def make_inputs(w: Workload, seed: int | None = None, poison: bool = False,
         num_blocks=num_blocks, k_cache=k_cache, v_cache=v_cache, q=q,
         key=key, value=value, slot_mapping=slots,
         scale=np.float32(1.0 / math.sqrt(D)), max_blocks=max_blocks,
+    )
+
+
+# Prefill (and chunked-prefill) batches: several query tokens per sequence,
+# causal over the sequence's cached positions.
+PREFILL_WORKLOADS: dict[str, Workload] = {
+    "prefill_qwen3": Workload(
+        "prefill_qwen3", 8, 16, 8, 128, 16, "bf16", ("uniform", 512, 2048),
+        max_blocks=128, seed=1101, query=("full",)),
+    "chunked_qwen3": Workload(
+        "chunked_qwen3", 8, 16, 8, 128, 16, "bf16", ("uniform", 1024, 4096),
+        max_blocks=256, seed=1102, query=("uniform", 128, 512)),
+    "prefill_llama32_1b": Workload(
+        "prefill_llama32_1b", 8, 32, 8, 64, 16, "bf16", ("uniform", 256, 2048),
+        max_blocks=128, seed=1103, query=("full",)),
+}
+
+
+def draw_query_lens(w: Workload, ctx: np.ndarray, rng: np.random.Generator) -> np.ndarray:
+    kind = w.query[0]
+    if kind == "full":
+        n = ctx.astype(np.int64)
+    elif kind == "uniform":
+        n = rng.integers(w.query[1], w.query[2], size=w.num_seqs, endpoint=True)
+    elif kind == "fixed":
+        n = np.asarray(w.query[1], dtype=np.int64)
+        assert n.size == w.num_seqs
+    else:
+        raise ValueError(kind)
+    return np.minimum(n, ctx).astype(np.int32)
+
+
+def make_prefill_inputs(w: Workload, seed: int | None = None, context_lens=None,
+                        query_lens=None) -> dict:
+    """Build one prefill (or chunked-prefill) batch.
+
+    Generation order: context lengths -> query lengths -> block permutation ->
+    K pool -> V pool -> q -> new key / value rows.  Sequence b brings
+    ``query_lens[b]`` new tokens, the last ones of its ``context_lens[b]``
+    positions; the positions before them (a cached prefix, possibly empty)
+    hold whatever the pool holds.
+
+    Returns numpy arrays: ``context_lens`` int32 [B], ``query_lens`` int32 [B],
+    ``query_start`` int32 [B+1] (sequence b's rows of q are
+    query_start[b] .. query_start[b+1]-1), ``block_tables`` int32
+    [B, max_blocks], ``k_cache``/``v_cache`` [num_blocks, bs, Hkv, D], ``q``
+    [T, Hq, D], ``key``/``value`` [T, Hkv, D] (the new tokens' rows),
+    ``slot_mapping`` int64 [T] (each new token's slot), ``scale`` and sizes.
+    """
+    assert w.query is not None, "not a prefill workload"
+    seed = w.seed if seed is None else seed
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, D, bs = (w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                         w.head_dim, w.block_size)
+    ctx = draw_context_lens(w, rng)
+    if context_lens is not None:
+        ctx = np.asarray(context_lens, dtype=np.int32).copy()
+    qlen = draw_query_lens(w, ctx, rng)
+    if query_lens is not None:
+        qlen = np.minimum(np.asarray(query_lens, dtype=np.int32), ctx)
+    max_blocks = w.max_blocks_per_seq
+    nblk = [-(-int(c) // bs) for c in ctx]
+    if max(nblk) > max_blocks:
+        raise ValueError("context longer than max_blocks * block_size")
+    num_blocks = pool_blocks(w, ctx)
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    tables = np.full((B, max_blocks), -1, dtype=np.int32)
+    cursor = 0
+    for b in range(B):
+        tables[b, :nblk[b]] = perm[cursor:cursor + nblk[b]]
+        cursor += nblk[b]
+
+    T = int(qlen.sum())
+    k_cache = _draw(rng, (num_blocks, bs, Hkv, D), w.sigma, w.dtype)
+    v_cache = _draw(rng, (num_blocks, bs, Hkv, D), w.sigma, w.dtype)
+    q = _draw(rng, (T, Hq, D), w.sigma, w.dtype)
+    key = _draw(rng, (T, Hkv, D), w.sigma, w.dtype)
+    value = _draw(rng, (T, Hkv, D), w.sigma, w.dtype)
+
+    start = np.zeros(B + 1, dtype=np.int32)
+    start[1:] = np.cumsum(qlen)
+    slots = np.empty(T, dtype=np.int64)
+    for b in range(B):
+        first = int(ctx[b]) - int(qlen[b])
+        for i in range(int(qlen[b])):
+            pos = first + i
+            slots[start[b] + i] = int(tables[b, pos // bs]) * bs + pos % bs
+
+    return dict(
+        workload=w, seed=seed, context_lens=ctx, query_lens=qlen, query_start=start,
+        block_tables=tables, num_blocks=num_blocks, k_cache=k_cache, v_cache=v_cache,
+        q=q, key=key, value=value, slot_mapping=slots,
+        scale=np.float32(1.0 / math.sqrt(D)), max_blocks=max_blocks,
+        max_query_len=int(qlen.max()) if B else 0,
     )

@@ -473,3 +473,102 @@ def pin_shared_prefix(dec, rac, w, members=(0, 1, 2), prefix_blocks=2):
     if not np.array_equal(out_shared, out_private):
         return False, "aliased prefix blocks change the result"
     return True, ""
+
+
+# ---------------------------------------------------------------- prefill
+def _prefill(pf, inp, **over):
+    args = dict(q=inp["q"], k_cache=inp["k_cache"], v_cache=inp["v_cache"],
+                block_tables=inp["block_tables"], context_lens=inp["context_lens"],
+                query_start=inp["query_start"], scale=inp["scale"],
+                dtype=inp["workload"].dtype)
+    args.update(over)
+    return pf(args["q"], args["k_cache"], args["v_cache"], args["block_tables"],
+              args["context_lens"], args["query_start"], args["scale"], args["dtype"])
+
+
+def written_prefill(inp, rac):
+    return rac(inp["key"], inp["value"], inp["k_cache"], inp["v_cache"],
+               inp["slot_mapping"])
+
+
+def pin_prefill_is_decode_per_token(pf, dec, rac, inp):
+    """P17: each new row equals a one-sequence decode whose context ends at
+    that row's position (prefill is decode repeated as the context grows)."""
+    k, v = written_prefill(inp, rac)
+    out = _prefill(pf, inp, k_cache=k, v_cache=v)
+    ctx, start = inp["context_lens"], inp["query_start"]
+    w = inp["workload"]
+    for b in range(len(ctx)):
+        n = int(start[b + 1] - start[b])
+        for i in range(n):
+            row = int(start[b]) + i
+            pos = int(ctx[b]) - n + i
+            ref = dec(inp["q"][row:row + 1], k, v, inp["block_tables"][b:b + 1],
+                      np.array([pos + 1], dtype=np.int32), inp["scale"], w.dtype)
+            if not np.array_equal(out[row], ref[0]):
+                return False, f"seq {b} row {i}"
+    return True, ""
+
+
+def pin_prefill_causal_sdpa(pf, rac, inp):
+    """P18: a whole-prompt prefill equals torch SDPA with is_causal=True
+    (CPU, float64) over the sequence's rows gathered chunk by chunk."""
+    import torch
+    k, v = written_prefill(inp, rac)
+    out = _prefill(pf, inp, k_cache=k, v_cache=v)
+    w = inp["workload"]
+    ctx, start = inp["context_lens"], inp["query_start"]
+    for b in range(len(ctx)):
+        L = int(ctx[b])
+        if int(start[b + 1] - start[b]) != L:
+            return False, "not a whole-prompt batch"
+        K = widen_ref(dense_from_chunks(k, inp["block_tables"][b], L), w.dtype)
+        V = widen_ref(dense_from_chunks(v, inp["block_tables"][b], L), w.dtype)
+        Q = widen_ref(inp["q"][int(start[b]):int(start[b + 1])], w.dtype)  # [L, Hq, D]
+        rep = w.num_q_heads // w.num_kv_heads
+        qt = torch.from_numpy(Q).permute(1, 0, 2).unsqueeze(0)
+        kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(rep, dim=0).unsqueeze(0)
+        vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(rep, dim=0).unsqueeze(0)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt.contiguous(), kt.contiguous(), vt.contiguous(), is_causal=True,
+            scale=float(np.float32(inp["scale"]))).squeeze(0).permute(1, 0, 2).numpy()
+        if not np.allclose(out[int(start[b]):int(start[b + 1])], ref, rtol=1e-12, atol=1e-12):
+            return False, f"seq {b}: max diff {np.abs(out[int(start[b]):int(start[b+1])] - ref).max()}"
+    return True, ""
+
+
+def pin_prefill_chunk_equals_tail(pf, rac, inp, tail):
+    """P19: prefilling only the last ``tail[b]`` tokens of each prompt (a chunk
+    after a cached prefix) gives exactly the last ``tail[b]`` rows of the
+    whole-prompt prefill.  ``inp`` is a whole-prompt batch."""
+    k, v = written_prefill(inp, rac)
+    full = _prefill(pf, inp, k_cache=k, v_cache=v)
+    start = inp["query_start"]
+    rows, st = [], [0]
+    for b in range(len(start) - 1):
+        hi = int(start[b + 1])
+        n = min(int(tail[b]), hi - int(start[b]))
+        rows.extend(range(hi - n, hi))
+        st.append(st[-1] + n)
+    rows = np.array(rows, dtype=np.int64)
+    out = _prefill(pf, inp, q=inp["q"][rows], k_cache=k, v_cache=v,
+                   query_start=np.array(st, dtype=np.int32))
+    if not np.array_equal(out, full[rows]):
+        return False, "chunk rows differ from the whole prompt's"
+    return True, ""
+
+
+def pin_prefill_first_token(pf, rac, w):
+    """P20: a one-token prompt attends to itself only: its output is exactly
+    its own V row (softmax of one score is 1)."""
+    ctx = np.ones(w.num_seqs, dtype=np.int32)
+    inp = synth.make_prefill_inputs(w, context_lens=ctx, query_lens=ctx)
+    k, v = written_prefill(inp, rac)
+    out = _prefill(pf, inp, k_cache=k, v_cache=v)
+    G = w.num_q_heads // w.num_kv_heads
+    for b in range(w.num_seqs):
+        vrow = widen_ref(inp["value"][b], w.dtype)
+        for h in range(w.num_q_heads):
+            if not np.array_equal(out[b, h], vrow[h // G]):
+                return False, f"b={b} h={h}"
+    return True, ""

@@ -213,3 +213,45 @@ def test_copy_mutant_is_caught(kind):
     ok, _ = P.pin_copy_blocks(copy, inp, pairs)
     assert not ok
 
+
+
+def _prefill_factory(kind):
+    def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, dtype):
+        scale = np.float64(np.float32(scale))
+        qf = PA.widen(q, dtype)
+        out = np.zeros(qf.shape)
+        bs = k_cache.shape[1]
+        for b in range(len(context_lens)):
+            L = int(context_lens[b])
+            lo, hi = int(query_start[b]), int(query_start[b + 1])
+            n = hi - lo
+            pos = np.arange(L)
+            phys = block_tables[b, pos // bs].astype(np.int64)
+            K = PA.widen(k_cache[phys, pos % bs], dtype)
+            V = PA.widen(v_cache[phys, pos % bs], dtype)
+            for i in range(n):
+                p = L - n + i
+                end = {"offset_from_zero": i + 1, "excludes_self": p,
+                       "one_ahead": min(L, p + 2), "not_causal": L}.get(kind, p + 1)
+                out[lo + i] = PA.decode_one(qf[lo + i], K[:end], V[:end], scale)
+        return out
+    return prefill
+
+
+PF_W = synth.Workload("pf_gqa2_bf16", 3, 4, 2, 32, 16, "bf16", ("uniform", 20, 70),
+                      seed=31, query=("uniform", 2, 40))
+PF_FULL = synth.Workload("pf_full_f32", 2, 2, 2, 16, 16, "f32", ("uniform", 10, 40),
+                         seed=32, query=("full",))
+
+
+@pytest.mark.parametrize("kind", ["offset_from_zero", "excludes_self", "one_ahead",
+                                  "not_causal"])
+def test_prefill_mutant_is_caught(kind):
+    pf = _prefill_factory(kind)
+    results = [
+        P.pin_prefill_is_decode_per_token(pf, oracle.decode, oracle.reshape_and_cache,
+                                          synth.make_prefill_inputs(PF_W)),
+        P.pin_prefill_causal_sdpa(pf, oracle.reshape_and_cache,
+                                  synth.make_prefill_inputs(PF_FULL)),
+    ]
+    assert not all(ok for ok, _ in results)

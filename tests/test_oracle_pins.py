@@ -185,3 +185,54 @@ def test_p16_shared_prefix(name, prefix_blocks):
     assert len(members) >= 2
     _ok(P.pin_shared_prefix(oracle.decode, oracle.reshape_and_cache, w, members,
                             prefix_blocks))
+
+
+# ------------------------------------------------------------ prefill
+PREFILL = {
+    "pf_gqa2_bf16": synth.Workload("pf_gqa2_bf16", 3, 4, 2, 32, 16, "bf16",
+                                   ("uniform", 20, 70), seed=31, query=("uniform", 1, 40)),
+    "pf_full_f32": synth.Workload("pf_full_f32", 2, 2, 2, 16, 16, "f32",
+                                  ("uniform", 10, 40), seed=32, query=("full",)),
+    "pf_mqa_bf16_bs32": synth.Workload("pf_mqa_bf16_bs32", 2, 4, 1, 16, 32, "bf16",
+                                       ("uniform", 30, 80), seed=33,
+                                       query=("uniform", 1, 30)),
+    "pf_full_gqa4_bf16": synth.Workload("pf_full_gqa4_bf16", 2, 8, 2, 32, 16, "bf16",
+                                        ("uniform", 17, 50), seed=34, query=("full",)),
+}
+
+
+@pytest.mark.parametrize("name", list(PREFILL))
+def test_p17_prefill_is_decode_per_token(name):
+    inp = synth.make_prefill_inputs(PREFILL[name])
+    _ok(P.pin_prefill_is_decode_per_token(oracle.prefill, oracle.decode,
+                                          oracle.reshape_and_cache, inp))
+
+
+@pytest.mark.parametrize("name", ["pf_full_f32", "pf_full_gqa4_bf16"])
+def test_p18_prefill_causal_sdpa(name):
+    inp = synth.make_prefill_inputs(PREFILL[name])
+    _ok(P.pin_prefill_causal_sdpa(oracle.prefill, oracle.reshape_and_cache, inp))
+
+
+@pytest.mark.parametrize("name", ["pf_full_f32", "pf_full_gqa4_bf16"])
+def test_p19_prefill_chunk_equals_tail(name):
+    inp = synth.make_prefill_inputs(PREFILL[name])
+    tail = [5, 11]
+    _ok(P.pin_prefill_chunk_equals_tail(oracle.prefill, oracle.reshape_and_cache, inp, tail))
+
+
+@pytest.mark.parametrize("name", ["pf_gqa2_bf16", "pf_full_f32"])
+def test_p20_prefill_first_token(name):
+    _ok(P.pin_prefill_first_token(oracle.prefill, oracle.reshape_and_cache, PREFILL[name]))
+
+
+def test_prefill_query_longer_than_context_is_nan():
+    w = PREFILL["pf_gqa2_bf16"]
+    inp = synth.make_prefill_inputs(w)
+    start = inp["query_start"]
+    ctx = inp["context_lens"].copy()
+    ctx[1] = int(start[2] - start[1]) - 1
+    out = oracle.prefill(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                         ctx, start, inp["scale"], w.dtype)
+    assert np.isnan(out[start[1]:start[2]]).all()
+    assert np.isfinite(out[start[0]:start[1]]).all()
