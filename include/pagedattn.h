@@ -96,6 +96,48 @@ pa_status pa_reshape_and_cache(const void* key, const void* value,
                                void* stream);
 
 /*
+ * Paged prefill (and chunked-prefill) attention, causal: the step before
+ * decode, where a prompt -- or a chunk of it after a cached prefix -- is
+ * processed at once (MinivLLM article, "Engine Layout": prefilling vs
+ * decoding; nano-vllm overview, "Prefill vs. Decode").
+ *
+ * Sequence b brings n_b = query_start[b+1] - query_start[b] new tokens, the
+ * last n_b of its L_b = context_lens[b] positions; their K/V rows must
+ * already be in the cache (pa_reshape_and_cache).  Row t of q for sequence
+ * b (t < n_b) sits at position L_b - n_b + t; for each query head h:
+ *
+ *   out[query_start[b] + t, h, :] = softmax_j(scale * q[., h, :] . K[j, h/G, :])
+ *                                   V[j, h/G, :]   over positions j <= L_b - n_b + t,
+ *
+ * with G = num_q_heads / num_kv_heads, float32 accumulation, bf16 output
+ * (round to nearest even).
+ *
+ *   out          [num_tokens, num_q_heads, head_dim]   (written)
+ *   q            [num_tokens, num_q_heads, head_dim]   (read)
+ *   k_cache, v_cache, block_tables, context_lens       as for the decode
+ *   query_start  [num_seqs + 1] int32, non-decreasing, query_start[0] = 0,
+ *                query_start[num_seqs] = num_tokens     (read)
+ *   max_query_len >= every n_b (sizes the launch; rows of a longer sequence
+ *                past max_query_len are left unwritten)
+ *
+ * bfloat16 only (PA_ERR_UNSUPPORTED for float32); head_dim in {64, 128},
+ * block_size in {16, 32}, G in {1, 2, 4, 8, 16, 32}.  No workspace.  Rows of
+ * a sequence with n_b > L_b, or whose L_b exceeds max_blocks_per_seq *
+ * block_size, are NaN; so are rows whose key range names a block outside the
+ * pool.  num_seqs, num_tokens or max_query_len of 0 is a no-op.
+ * Asynchronous on `stream`.
+ */
+pa_status pa_paged_attention_prefill(void* out, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens,
+                                     const int32_t* query_start, int32_t num_seqs,
+                                     int32_t num_tokens, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t num_blocks, int32_t block_size,
+                                     int32_t max_blocks_per_seq, int32_t max_query_len,
+                                     float scale, pa_dtype dtype, void* stream);
+
+/*
  * Block copy for copy-on-write of shared blocks.  Sequences that share a
  * prompt prefix may name the same physical block in their block tables
  * (block sharing and prefix caching: MinivLLM article, "Running It" section;

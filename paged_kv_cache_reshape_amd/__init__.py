@@ -75,6 +75,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.pa_paged_attention_decode.argtypes = [
             vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
             vp, sz, vp, i64, i32, vp]
+        lib.pa_paged_attention_prefill.restype = i32
+        lib.pa_paged_attention_prefill.argtypes = [
+            vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32,
+            i32, vp]
         lib.pa_copy_blocks.restype = i32
         lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
         lib.pa_debug_gather_kv.restype = i32
@@ -256,6 +260,53 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
             max_blocks, float(scale), partition_size, ws_ptr, ws_len, c_ptr, c_len, dt,
             _stream(dev))
     _check(st, "pa_paged_attention_decode")
+    return out
+
+
+def paged_attention_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: torch.Tensor,
+                            query_start: torch.Tensor, scale: float,
+                            max_query_len: int | None = None,
+                            out: torch.Tensor | None = None) -> torch.Tensor:
+    """Causal prefill attention ``out[T, Hq, D]`` over the paged caches.
+
+    Sequence b's new tokens are rows ``query_start[b] : query_start[b+1]`` of
+    ``q``, the last ones of its ``context_lens[b]`` positions (their K/V rows
+    already written).  ``max_query_len`` bounds the rows per sequence; if not
+    given it is read from ``query_start`` (a device-to-host copy).
+    """
+    lib = load_library()
+    dev = _same_device(q, k_cache, v_cache, block_tables, context_lens, query_start)
+    _need(q.dim() == 3, "q must be [T, Hq, D]")
+    T, hq, d = q.shape
+    _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape,
+          "caches must be [num_blocks, block_size, Hkv, D] and alike")
+    nb, bs, hkv, d2 = k_cache.shape
+    _need(d2 == d, "head_dim of q and cache differ")
+    B = context_lens.shape[0]
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == B, "block_tables must be int32 [B, max_blocks]")
+    _need(context_lens.dtype == torch.int32 and context_lens.dim() == 1,
+          "context_lens must be int32 [B]")
+    _need(query_start.dtype == torch.int32 and query_start.shape == (B + 1,),
+          "query_start must be int32 [B + 1]")
+    dt = _dtype_code(q)
+    _need(k_cache.dtype == v_cache.dtype == q.dtype, "dtype mismatch")
+    if max_query_len is None:
+        qs = query_start.cpu()
+        max_query_len = int((qs[1:] - qs[:-1]).max()) if B else 0
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _same_device(out)
+        _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    with torch.cuda.device(dev):
+        st = lib.pa_paged_attention_prefill(
+            out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(), B, T,
+            hq, hkv, d, nb, bs, block_tables.shape[1], int(max_query_len), float(scale), dt,
+            _stream(dev))
+    _check(st, "pa_paged_attention_prefill")
     return out
 
 

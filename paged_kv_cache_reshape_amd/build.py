@@ -25,7 +25,8 @@ LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 ARCH = "gfx950"
-HIP_SOURCES = ["decode_api.hip", "decode_partition.hip", "decode_mfma.hip", "kv_write.hip"]
+HIP_SOURCES = ["decode_api.hip", "decode_partition.hip", "decode_mfma.hip", "prefill_mfma.hip",
+               "kv_write.hip"]
 HOST_SOURCES = ["status.cpp"]
 
 HIPCC_FLAGS = [

@@ -1,0 +1,252 @@
+// Matrix-core attention over 16-token tiles of K/V staged in LDS, shared by
+// the large-group decode kernel and the prefill kernel.
+//
+// A wave holds NR query rows (query heads of one token for the decode;
+// (token, head) pairs for the prefill) and folds one K/V block at a time
+// into their online-softmax state:
+//
+//   * S^T = K q^T with v_mfma_f32_16x16x32_bf16: A = K rows read back from
+//     LDS one token per lane, B = the query rows held in registers.  C's
+//     register r in lane (j, n) is then the score of row n of the 16-row tile
+//     against token 4j + r of the 16-token tile;
+//   * each score is kept when its key position is at most the row's own
+//     position (the decode's rows all sit at the last position; prefill rows
+//     are causal), else it becomes -inf;
+//   * online softmax per row in that layout (block maximum by two lane swaps),
+//     with a lazy maximum: the kept maximum moves only when a score of the
+//     block passes it by more than 8 (base 2), so every weight is at most 256
+//     and most blocks rescale nothing.  The algebra is the online softmax of
+//     the pages (barellm README, paged-cache list; LLAISYS README,
+//     self-attention item); the final division by the running sum removes the
+//     choice of kept maximum;
+//   * O += P V with the same MFMA: C of the first product is already laid out
+//     as the A operand (lane (j, n): row n, tokens 4j .. 4j+3); V arrives
+//     transposed from LDS through ds_read_b64_tr_b16, which gives lane (j, n)
+//     the values of tokens 4j .. 4j+3 at one d.  P is split as
+//     bf16(p) + bf16(p - bf16(p)), two products, so the weights keep 16
+//     significant bits (one bf16 rounding of p costs up to 2^-9 relative per
+//     weight, more than the output tolerance allows).
+#pragma once
+
+#include "attn_common.hpp"
+
+namespace pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource word 3 for gfx9-family raw buffer loads (32-bit data
+// format; accesses are range-checked against num_records bytes).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+template <int D, int BS, int NR>
+struct TileShape {
+  static constexpr int RL = D * 2 / 16;     // lanes per token row in a 16-byte global load
+  static constexpr int ROWS = 64 / RL;      // token rows per wave-wide global load
+  static constexpr int NI = BS / ROWS;      // wave-wide global loads per block, K or V
+  static constexpr int TPB = BS / 16;       // 16-token tiles per block
+  static constexpr int HT = (NR + 15) / 16; // 16-row tiles of query rows
+  static constexpr int DK = D / 32;         // 32-wide d chunks of q.k
+  static constexpr int DT = D / 16;         // 16-wide d tiles of p.v
+  static constexpr int PITCH = D * 2 + 16;  // LDS row pitch, bytes (padding spreads banks)
+  static constexpr int TILE = BS * PITCH;   // one of K or V for one block
+};
+
+__device__ __forceinline__ float max4(f32x4 v) {
+  return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+}
+
+// Online-softmax state of one wave for NR query rows.
+template <int D, int BS, int NR>
+struct RowTileAttn {
+  using Sh = TileShape<D, BS, NR>;
+  static constexpr int TPB = Sh::TPB, HT = Sh::HT, DK = Sh::DK, DT = Sh::DT;
+  static constexpr int PITCH = Sh::PITCH;
+  static constexpr float kLazy = 8.0f;
+
+  bf16x8 qb[HT][DK];  // B operand of q.k: lane (j, n) holds row 16 ht + n, d = 32 i + 8 j ..
+  f32x4 o[HT][DT];    // lane (j, n): output of row 16 ht + 4 j + r at d = 16 dt + n
+  float m[HT], mth[HT], l[HT];  // lane (j, n): row 16 ht + n (l: this lane's tokens only)
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      m[ht] = kNoMax;
+      mth[ht] = kNoMax;
+      l[ht] = 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[ht][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  }
+
+  // row_ptr(r): element pointer to query row r (D values), or nullptr for a
+  // row that does not exist (it is then zero and every score of it masked).
+  template <class RowPtr>
+  __device__ __forceinline__ void load_q(RowPtr&& row_ptr, int lane) {
+    const int n = lane & 15, j = lane >> 4;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const uint16_t* p = row_ptr(16 * ht + n);
+#pragma unroll
+      for (int i = 0; i < DK; ++i) {
+        const uint4 v = p ? load_chunk(p + 32 * i + 8 * j) : make_uint4(0, 0, 0, 0);
+        qb[ht][i] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+  }
+
+  // Rescale row tile ht to the new kept maximum mn (per lane = per row n).
+  __device__ __forceinline__ void rescale(int ht, float mn, int lane) {
+    const float alpha = fast_exp2(m[ht] - mn);
+    l[ht] *= alpha;
+    m[ht] = mn;
+    mth[ht] = mn + kLazy;
+    // o's register r of lane (j, n) belongs to row 4j + r: take that row's
+    // factor from lane 4j + r (group 0 holds every row's factor).
+    const int j = lane >> 4;
+    float f[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      f[r] = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * j + r) * 4, __float_as_int(alpha)));
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[ht][dt][r] *= f[r];
+  }
+
+  // One block, staged in LDS at kt / vt (rows of PITCH bytes, token-major,
+  // every row finite).  pos0: sequence position of the block's first token;
+  // rowpos[ht]: this lane's row position (lane (j, n) -> row 16 ht + n);
+  // keys past a row's position are masked (a row position of -1 masks all).
+  // All scores of the block are formed first, so that one kept maximum per
+  // row serves every weight of the block.
+  __device__ __forceinline__ void consume(const char* kt, const char* vt, int pos0,
+                                          const int (&rowpos)[HT], float scale_log2, int lane) {
+    const int n = lane & 15, j = lane >> 4;
+    f32x4 x[HT][TPB];
+#pragma unroll
+    for (int tt = 0; tt < TPB; ++tt) {
+      bf16x8 ka[DK];
+#pragma unroll
+      for (int i = 0; i < DK; ++i)
+        ka[i] = *reinterpret_cast<const bf16x8*>(kt + (tt * 16 + n) * PITCH + (32 * i + 8 * j) * 2);
+      const int kp = pos0 + tt * 16 + 4 * j;  // key position of register 0
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < DK; ++i)
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i], qb[ht][i], s, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          x[ht][tt][r] = kp + r <= rowpos[ht] ? s[r] * scale_log2 : -INFINITY;
+      }
+    }
+    bf16x4 ph[HT][TPB], pl[HT][TPB];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      float bmax = max4(x[ht][0]);
+#pragma unroll
+      for (int tt = 1; tt < TPB; ++tt) bmax = fmaxf(bmax, max4(x[ht][tt]));
+      bmax = fmaxf(bmax, lane_xor<16>(bmax));
+      bmax = fmaxf(bmax, lane_xor<32>(bmax));
+      if (__builtin_amdgcn_ballot_w64(bmax > mth[ht]) != 0)
+        rescale(ht, fmaxf(m[ht], bmax), lane);
+      float sum = 0.0f;
+#pragma unroll
+      for (int tt = 0; tt < TPB; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(x[ht][tt][r] - m[ht]);
+          sum += p;
+          const __bf16 hi = static_cast<__bf16>(p);
+          ph[ht][tt][r] = hi;
+          pl[ht][tt][r] = static_cast<__bf16>(p - static_cast<float>(hi));
+        }
+      l[ht] += sum;
+    }
+    // O += P V, one 16-wide d tile at a time; V arrives transposed from LDS.
+    const int L = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      bf16x4 vb[TPB];
+#pragma unroll
+      for (int tt = 0; tt < TPB; ++tt) {
+        const char* p = vt + (tt * 16 + 4 * j + (L >> 2)) * PITCH + (16 * dt + 4 * (L & 3)) * 2;
+        vb[tt] = __builtin_bit_cast(
+            bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4*)(p)));
+      }
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        if constexpr (TPB == 2) {
+          const bf16x8 b = __builtin_shufflevector(vb[0], vb[1], 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 ah = __builtin_shufflevector(ph[ht][0], ph[ht][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 al = __builtin_shufflevector(pl[ht][0], pl[ht][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, o[ht][dt], 0, 0, 0);
+          o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, o[ht][dt], 0, 0, 0);
+        } else {
+          const s16x4 b = __builtin_bit_cast(s16x4, vb[0]);
+          o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              __builtin_bit_cast(s16x4, ph[ht][0]), b, o[ht][dt], 0, 0, 0);
+          o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              __builtin_bit_cast(s16x4, pl[ht][0]), b, o[ht][dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // Row sums over all of the wave's tokens: lane (j, n) gets row 16 ht + n's.
+  __device__ __forceinline__ float row_sum(int ht) const {
+    float t = l[ht];
+    t += lane_xor<16>(t);
+    t += lane_xor<32>(t);
+    return t;
+  }
+
+  // Write the wave's state to LDS: s_acc[row][d], s_m[row], s_l[row], rows < NR.
+  __device__ __forceinline__ void to_lds(float (*s_acc)[D], float* s_m, float* s_l, int lane) {
+    const int n = lane & 15, j = lane >> 4;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const float t = row_sum(ht);
+      const int h = 16 * ht + n;
+      if (j == 0 && h < NR) {
+        s_m[h] = m[ht];
+        s_l[h] = t;
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int hh = 16 * ht + 4 * j + r;
+          if (hh < NR) s_acc[hh][16 * dt + n] = o[ht][dt][r];
+        }
+    }
+  }
+
+  // Normalised output of every row: store(row, d, value) for rows < NR.
+  template <class Store>
+  __device__ __forceinline__ void store_rows(Store&& store, int lane) const {
+    const int n = lane & 15, j = lane >> 4;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const float t = row_sum(ht);
+      float rs[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        rs[r] = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * j + r) * 4, __float_as_int(t)));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * ht + 4 * j + r;
+          if (row < NR) store(row, 16 * dt + n, o[ht][dt][r] / rs[r]);
+        }
+    }
+  }
+};
+
+}  // namespace pa

@@ -106,6 +106,30 @@ def test_copy_blocks_argument_checks(lib):
     assert f(16, 16, 16, 3, 0, 64, 32, 16, 0, None) == INVALID
 
 
+def test_prefill_argument_checks(lib):
+    f = lib.pa_paged_attention_prefill
+
+    def call(**kw):
+        a = dict(out=16, q=16, k=16, v=16, bt=16, cl=16, qs=16, B=2, T=8, Hq=4, Hkv=2, D=64,
+                 nb=32, bs=16, mb=4, mq=4, scale=0.125, dt=1)
+        a.update(kw)
+        return f(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"], a["B"], a["T"],
+                 a["Hq"], a["Hkv"], a["D"], a["nb"], a["bs"], a["mb"], a["mq"], a["scale"],
+                 a["dt"], None)
+    assert call(dt=0) == UNSUPPORTED            # float32 prefill is not built
+    assert call(dt=7) == INVALID
+    assert call(Hq=6, Hkv=2) == UNSUPPORTED     # group of 3
+    assert call(Hq=6, Hkv=4) == INVALID
+    assert call(D=96) == UNSUPPORTED
+    assert call(bs=64) == UNSUPPORTED
+    assert call(T=-1) == INVALID
+    assert call(qs=None) == INVALID
+    assert call(q=24) == INVALID                # misaligned
+    assert call(mq=1 << 30) == INVALID          # launch too large
+    assert call(T=0, q=None, out=None) == OK    # nothing to do
+    assert call(B=0, qs=None) == OK
+
+
 def test_gather_argument_checks(lib):
     f = lib.pa_debug_gather_kv
     assert f(16, 16, 16, 16, 16, 16, 0, 2, 64, 32, 16, 4, 0, None) == OK
@@ -178,3 +202,4 @@ def test_ctypes_signatures_match_header(lib):
     assert len(lib.pa_reshape_and_cache.argtypes) == 12
     assert len(lib.pa_debug_gather_kv.argtypes) == 14
     assert len(lib.pa_copy_blocks.argtypes) == 10
+    assert len(lib.pa_paged_attention_prefill.argtypes) == 19

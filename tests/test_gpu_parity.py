@@ -508,3 +508,116 @@ def test_prior_art_baseline_matches_oracle(name):
                                          d["block_tables"], d["context_lens"], d["scale"])
     ref, _ = oracle_step(inp)
     G.assert_close(G.host_f64(out), ref, w.dtype, f"{name} baseline")
+
+
+# ------------------------------------------------------------------ prefill
+PF = {
+    "pf_g2_d128_bs16": synth.Workload("pf_g2_d128_bs16", 4, 8, 4, 128, 16, "bf16",
+                                      ("uniform", 100, 400), seed=51,
+                                      query=("uniform", 1, 300)),
+    "pf_full_g1_d128_bs32": synth.Workload("pf_full_g1_d128_bs32", 3, 4, 4, 128, 32, "bf16",
+                                           ("uniform", 50, 300), seed=52, query=("full",)),
+    "pf_g4_d64_bs16": synth.Workload("pf_g4_d64_bs16", 3, 16, 4, 64, 16, "bf16",
+                                     ("uniform", 60, 500), seed=53,
+                                     query=("uniform", 20, 500)),
+    "pf_full_g8_d64_bs32": synth.Workload("pf_full_g8_d64_bs32", 2, 16, 2, 64, 32, "bf16",
+                                          ("uniform", 30, 200), seed=54, query=("full",)),
+    "pf_g16_d128_bs16": synth.Workload("pf_g16_d128_bs16", 2, 16, 1, 128, 16, "bf16",
+                                       ("uniform", 40, 150), seed=55,
+                                       query=("uniform", 1, 150)),
+    "pf_full_g32_d128_bs32": synth.Workload("pf_full_g32_d128_bs32", 2, 32, 1, 128, 32,
+                                            "bf16", ("uniform", 20, 90), seed=56,
+                                            query=("full",)),
+}
+
+
+def prefill_gpu(inp):
+    """KV write of the new tokens, then prefill, on the GPU."""
+    d = G.upload(inp)
+    d["query_start"] = torch.from_numpy(inp["query_start"]).cuda()
+    pa.reshape_and_cache(d["key"], d["value"], d["k_cache"], d["v_cache"], d["slot_mapping"])
+    out = pa.paged_attention_prefill(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                     d["context_lens"], d["query_start"], d["scale"])
+    return d, out
+
+
+def prefill_oracle(inp):
+    k, v = oracle.reshape_and_cache(inp["key"], inp["value"], inp["k_cache"],
+                                    inp["v_cache"], inp["slot_mapping"])
+    return oracle.prefill(inp["q"], k, v, inp["block_tables"], inp["context_lens"],
+                          inp["query_start"], inp["scale"], inp["workload"].dtype), (k, v)
+
+
+@pytest.mark.parametrize("name", list(PF))
+def test_prefill_matches_oracle(name):
+    w = PF[name]
+    inp = synth.make_prefill_inputs(w)
+    say("prefill", name, "rows", int(inp["query_start"][-1]) * (w.num_q_heads // w.num_kv_heads))
+    d, out = prefill_gpu(inp)
+    ref, (k_ref, _) = prefill_oracle(inp)
+    assert np.array_equal(G.host_storage(d["k_cache"]), k_ref)
+    G.assert_close(G.host_f64(out), ref, "bf16", name)
+
+
+def test_prefill_ragged_with_empty_and_bad_sequences():
+    """A sequence with no new tokens writes nothing; a sequence claiming more
+    new tokens than positions gets NaN rows; the others are unaffected."""
+    w = PF["pf_g2_d128_bs16"]
+    inp = synth.make_prefill_inputs(w, query_lens=np.array([37, 0, 250, 5], dtype=np.int32))
+    ctx = inp["context_lens"].copy()
+    start = inp["query_start"]
+    say("prefill ragged/bad")
+    d = G.upload(inp)
+    d["query_start"] = torch.from_numpy(start).cuda()
+    pa.reshape_and_cache(d["key"], d["value"], d["k_cache"], d["v_cache"], d["slot_mapping"])
+    bad = 3
+    ctx_bad = ctx.copy()
+    ctx_bad[bad] = int(start[bad + 1] - start[bad]) - 1   # fewer positions than new rows
+    out = pa.paged_attention_prefill(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                     torch.from_numpy(ctx_bad).cuda(), d["query_start"],
+                                     d["scale"])
+    got = G.host_f64(out)
+    ref, _ = prefill_oracle(inp)
+    ok = slice(0, int(start[bad]))
+    G.assert_close(got[ok], ref[ok], "bf16", "good sequences")
+    assert np.isnan(got[int(start[bad]):int(start[bad + 1])]).all()
+
+
+@pytest.mark.parametrize("name", ["pf_g2_d128_bs16", "pf_full_g32_d128_bs32",
+                                  "pf_g4_d64_bs16"])
+def test_prefill_first_token_exact(name):
+    """P20 on the GPU: a one-token prompt returns exactly its own V row."""
+    w = PF[name]
+    one = np.ones(w.num_seqs, dtype=np.int32)
+    inp = synth.make_prefill_inputs(w, context_lens=one, query_lens=one)
+    say("prefill one-token prompts", name)
+    _, out = prefill_gpu(inp)
+    got = G.host_storage(out)
+    grp = w.num_q_heads // w.num_kv_heads
+    for b in range(w.num_seqs):
+        assert np.array_equal(got[b], np.repeat(inp["value"][b], grp, axis=0)), b
+
+
+@pytest.mark.parametrize("name", list(synth.PREFILL_WORKLOADS))
+def test_prefill_workload_sampled(name):
+    """The benchmark prefill batches at full size: every row of every sequence
+    is computed on the GPU; sampled rows are checked one by one against the
+    oracle's decode ending at the row's position (P17)."""
+    w = synth.PREFILL_WORKLOADS[name]
+    inp = synth.make_prefill_inputs(w)
+    say("prefill workload", name, "tokens", int(inp["query_start"][-1]))
+    d, out = prefill_gpu(inp)
+    got = G.host_f64(out)
+    assert np.isfinite(got).all()
+    k, v = oracle.reshape_and_cache(inp["key"], inp["value"], inp["k_cache"],
+                                    inp["v_cache"], inp["slot_mapping"])
+    rng = np.random.default_rng(9)
+    ctx, start = inp["context_lens"], inp["query_start"]
+    for b in range(w.num_seqs):
+        n = int(start[b + 1] - start[b])
+        for i in sorted(set(rng.integers(0, n, size=6).tolist()) | {0, n - 1}):
+            row = int(start[b]) + i
+            pos = int(ctx[b]) - n + i
+            ref = oracle.decode(inp["q"][row:row + 1], k, v, inp["block_tables"][b:b + 1],
+                                np.array([pos + 1], dtype=np.int32), inp["scale"], w.dtype)
+            G.assert_close(got[row:row + 1], ref, w.dtype, f"{name} seq {b} row {i}")
