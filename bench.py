@@ -157,12 +157,160 @@ def cpu_baseline(inp: dict, budget_s: float) -> dict:
                        f"({dt:.1f} s, {done_bytes / 1e6:.1f} MB of KV rows)")}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+
+
+def prefill_flops(inp: dict) -> int:
+    """Attention flops of one prefill launch: each new row at position p
+    does q.k and p.v over p + 1 keys, 2 * D flops each, for every query head."""
+    w = inp["workload"]
+    ctx, start = inp["context_lens"].astype(np.int64), inp["query_start"].astype(np.int64)
+    n = start[1:] - start[:-1]
+    # sum over rows of (p + 1) with p = ctx - n + i, i < n
+    keys = (n * (ctx - n) + n * (n + 1) // 2).sum()
+    return int(4 * w.num_q_heads * w.head_dim * keys)
+
+
+def prefill_cpu_baseline(inp: dict, budget_s: float) -> dict:
+    """Time the float64 oracle's prefill on the batch's first sequences."""
+    import oracle
+    w = inp["workload"]
+    ctx, start = inp["context_lens"], inp["query_start"]
+    k, v = oracle.reshape_and_cache(inp["key"], inp["value"], inp["k_cache"],
+                                    inp["v_cache"], inp["slot_mapping"])
+    flops, rows, t0 = 0, 0, time.perf_counter()
+    for b in range(len(ctx)):
+        lo, hi = int(start[b]), int(start[b + 1])
+        for i in range(hi - lo):
+            one = np.array([0, 1], dtype=np.int32)
+            pos = int(ctx[b]) - (hi - lo) + i
+            oracle.prefill(inp["q"][lo + i:lo + i + 1], k, v, inp["block_tables"][b:b + 1],
+                           np.array([pos + 1], dtype=np.int32), one, inp["scale"], w.dtype)
+            flops += 4 * w.num_q_heads * w.head_dim * (pos + 1)
+            rows += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle prefill, the first {rows} new tokens of the "
+                      f"batch in order ({dt:.1f} s)"}
+
+
+def run_prefill(args, torch, pa) -> int:
+    """Prefill step: write every new token's K/V rows, then causal prefill
+    attention over the paged cache.  value = attention TFLOP/s of the step."""
+    w = synth.PREFILL_WORKLOADS[args.workload]
+    inp = synth.make_prefill_inputs(w)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    pool_bytes = 2 * inp["k_cache"].nbytes
+    R = args.replicas or min(64, max(1, math.ceil(1.25 * 2**30 / pool_bytes)))
+    kcs = [up(inp["k_cache"])]
+    vcs = [up(inp["v_cache"])]
+    kcs += [kcs[0].clone() for _ in range(R - 1)]
+    vcs += [vcs[0].clone() for _ in range(R - 1)]
+    q, key, value = up(inp["q"]), up(inp["key"]), up(inp["value"])
+    tables, lens = up(inp["block_tables"]), up(inp["context_lens"])
+    qstart, slots = up(inp["query_start"]), up(inp["slot_mapping"])
+    scale = float(inp["scale"])
+    out = torch.empty_like(q)
+    mq = int(inp["max_query_len"])
+    stream = torch.cuda.current_stream(dev)
+
+    def write(i):
+        pa.reshape_and_cache(key, value, kcs[i % R], vcs[i % R], slots)
+
+    def attn(i):
+        pa.paged_attention_prefill(q, kcs[i % R], vcs[i % R], tables, lens, qstart, scale,
+                                   max_query_len=mq, out=out)
+
+    def step(i):
+        write(i)
+        attn(i)
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    steps = min(args.steps, 200)
+    warm = min(args.warmup, 20)
+    for i in range(warm):
+        step(i)
+    ms_step = timed(step, steps)
+    ms_attn = timed(attn, steps)
+    ms_write = timed(write, steps)
+    flops = prefill_flops(inp)
+    T = int(inp["query_start"][-1])
+    achieved = flops / (ms_attn / 1e3) / 1e12
+    res = {
+        "metric": "prefill attention TFLOP/s (causal, paged cache)",
+        "value": round(flops / (ms_step / 1e3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{w.name}: B={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+                         f"D={w.head_dim} block_size={w.block_size} ctx {w.ctx} "
+                         f"new tokens {w.query} {w.dtype}"),
+            "new_tokens": T,
+            "sum_ctx": int(inp["context_lens"].sum()),
+            "kv_pool_replicas": R,
+            "step": "reshape_and_cache (all new tokens) + paged_attention_prefill",
+        },
+        "tokens_per_s": round(T / (ms_step / 1e3), 1),
+        "prefill_us_mean": round(ms_attn * 1e3, 3),
+        "write_us_mean": round(ms_write * 1e3, 3),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "prefill_mfma_kernel",
+            "flops_per_launch": flops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = prefill_cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="qwen3_0p6b", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--workload", default="qwen3_0p6b",
+                    choices=sorted(synth.WORKLOADS) + sorted(synth.PREFILL_WORKLOADS),
+                    help="a decode batch, or a prefill batch (prefill_*, chunked_*)")
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="tokens per partition; -1 = the workload's, 0 = library choice")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for 1.25 GiB")
@@ -185,6 +333,8 @@ def main() -> int:
         from paged_kv_cache_reshape_amd import build as _b
         _b.build()
     pa.load_library()
+    if args.workload in synth.PREFILL_WORKLOADS:
+        return run_prefill(args, torch, pa)
 
     w = synth.WORKLOADS[args.workload]
     ps = w.partition_size if args.partition_size < 0 else args.partition_size
