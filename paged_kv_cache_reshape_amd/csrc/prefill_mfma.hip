@@ -14,9 +14,9 @@
 // of one (sequence, kv head); rows of later tokens see more keys, so the
 // grid's row groups are issued last-first.  Per K/V block (the blocks up to
 // the workgroup's last row position):
-//   * the whole workgroup loads the block's K and V rows for kv head g with
-//     full-row coalesced 16-byte loads into one of two LDS stages (the next
-//     block's loads are in flight while the current one is used);
+//   * the whole workgroup loads 64 keys' worth of blocks (K and V rows for kv
+//     head g) with full-row coalesced 16-byte loads into one of two LDS stages
+//     (the next stage's loads are in flight while the current one is used);
 //   * every wave folds the block into its rows' online-softmax state
 //     (mfma_attn.hpp), each score masked past its row's position; a wave
 //     whose rows all end before the block skips it.
@@ -48,18 +48,28 @@ struct PrefillArgs {
 
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillRows = 32;  // query rows per wave
+// Keys per LDS stage (several blocks): 64, or 32 at head_dim 64, where the
+// workgroup is held to 128 VGPRs so that two fit on a compute unit.
+template <int D>
+constexpr int prefill_stage_keys() { return D == 64 ? 32 : 64; }
 
 template <int D, int BS, int G, int NW>
-__global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int NR = kPrefillRows;
-  using Sh = TileShape<D, BS, NR>;
-  using T = RowTileAttn<D, BS, NR>;
-  constexpr int RL = Sh::RL, PITCH = Sh::PITCH, TILE = Sh::TILE, HT = Sh::HT;
+  constexpr int KC = 32;  // keys folded per call: two 16-token tiles, so p.v runs on
+                          // v_mfma_f32_16x16x32_bf16 whatever the block size
+  using Sh = TileShape<D, KC, NR>;
+  using T = RowTileAttn<D, KC, NR>;
+  constexpr int RL = Sh::RL, PITCH = Sh::PITCH, HT = Sh::HT;
   constexpr int NT = NW * 64;
   constexpr int kChunks = BS * RL;  // 16-byte chunks of one block's rows, K or V
   static_assert(kChunks % 64 == 0, "a wave's chunks are all K or all V");
-  constexpr int NCH = (2 * kChunks + NT - 1) / NT;  // chunks per thread, K and V
-  __shared__ __attribute__((aligned(16))) char s_kv[2][2 * TILE];  // [stage][K | V]
+  constexpr int NCH = (2 * kChunks + NT - 1) / NT;  // chunks per thread per block, K and V
+  constexpr int KB = prefill_stage_keys<D>() / BS;              // blocks per stage
+  constexpr int SK = prefill_stage_keys<D>() * PITCH;           // one stage's K (or V) rows
+  // [stage][K rows | V rows]: the stage's KB blocks are consecutive logical
+  // blocks, so row t of a stage is key position (first block) * BS + t.
+  __shared__ __attribute__((aligned(16))) char s_kv[2][2 * SK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -119,56 +129,75 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a) {
   const char* vbase = static_cast<const char*>(a.v_cache);
   const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks;
   bool bad = false;  // a block id outside the pool: rows become NaN
-  uint4 r[NCH];
+  uint4 r[KB][NCH];
   auto chunk = [&](int i) { return (tid + i * NT) % (2 * kChunks); };
-  auto fetch = [&](int jb) {
-    int id = trow[jb];
-    const bool ok = id >= 0 && id < a.num_blocks;
-    bad = bad || !ok;
-    id = ok ? id : 0;
-    const size_t boff = (size_t)id * blk_bytes;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(kbase + boff), 0, blk_bytes, kBufferRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(vbase + boff), 0, blk_bytes, kBufferRsrcWord3);
-    const int pos0 = jb * BS;
+  // Loads of blocks jb0 .. jb0 + KB - 1 (ids past the last block read the last
+  // one again: in range, never folded in).
+  auto fetch = [&](int jb0) {
+    // Table entries first, all together: a vector load completes in order,
+    // so waiting for an entry between K/V loads would wait for those too.
+    int ids[KB];
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = chunk(i);
-      // A wave's 64 chunks are all K or all V (kChunks is a multiple of 64).
-      const bool is_k = __builtin_amdgcn_readfirstlane(c) < kChunks;
-      const int cc = is_k ? c : c - kChunks;
-      const int tok = cc / RL;
-      // Tokens at or past the context read the block's token 0 (finite).
-      const uint32_t off = head_off + 16u * (cc % RL) +
-                           (pos0 + tok < ctx ? (uint32_t)tok * tok_bytes : 0u);
-      r[i] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(is_k ? rk : rv, off, 0, 0));
+    for (int kb = 0; kb < KB; ++kb) ids[kb] = trow[jb0 + kb < nblk ? jb0 + kb : nblk - 1];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int jb = jb0 + kb < nblk ? jb0 + kb : nblk - 1;
+      int id = __builtin_amdgcn_readfirstlane(ids[kb]);
+      const bool ok = id >= 0 && id < a.num_blocks;
+      bad = bad || !ok;
+      id = ok ? id : 0;
+      const size_t boff = (size_t)id * blk_bytes;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(kbase + boff), 0, blk_bytes, kBufferRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(vbase + boff), 0, blk_bytes, kBufferRsrcWord3);
+      const int pos0 = jb * BS;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = chunk(i);
+        // A wave's 64 chunks are all K or all V (kChunks is a multiple of 64).
+        const bool is_k = __builtin_amdgcn_readfirstlane(c) < kChunks;
+        const int cc = is_k ? c : c - kChunks;
+        const int tok = cc / RL;
+        // Tokens at or past the context read the block's token 0 (finite).
+        const uint32_t off = head_off + 16u * (cc % RL) +
+                             (pos0 + tok < ctx ? (uint32_t)tok * tok_bytes : 0u);
+        r[kb][i] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(is_k ? rk : rv, off, 0, 0));
+      }
     }
   };
   auto stage = [&](int s) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = chunk(i);
-      const bool is_k = __builtin_amdgcn_readfirstlane(c) < kChunks;
-      const int cc = is_k ? c : c - kChunks;
-      *reinterpret_cast<uint4*>(s_kv[s] + (is_k ? 0 : TILE) + (cc / RL) * PITCH +
-                                (cc % RL) * 16) = r[i];
-    }
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = chunk(i);
+        const bool is_k = __builtin_amdgcn_readfirstlane(c) < kChunks;
+        const int cc = is_k ? c : c - kChunks;
+        *reinterpret_cast<uint4*>(s_kv[s] + (is_k ? 0 : SK) + (kb * BS + cc / RL) * PITCH +
+                                  (cc % RL) * 16) = r[kb][i];
+      }
   };
 
   fetch(0);
   stage(0);
-  __builtin_amdgcn_s_waitcnt(0);  // q rows and block 0 are in: nothing pending at the loop
+  __builtin_amdgcn_s_waitcnt(0);  // q rows and the first blocks are in: nothing pending
   __syncthreads();
-  for (int jb = 0; jb < nblk; ++jb) {
-    const int s = jb & 1;
-    // The next block's loads (the last block again at the end: in range,
-    // unused) are in flight while this one is folded in.
-    fetch(jb + 1 < nblk ? jb + 1 : jb);
+  for (int jb0 = 0; jb0 < nblk; jb0 += KB) {
+    const int s = (jb0 / KB) & 1;
+    // The next stage's loads are in flight while this one is folded in.
+    fetch(jb0 + KB < nblk ? jb0 + KB : jb0);
     __builtin_amdgcn_sched_barrier(0);
-    if (jb * BS < wave_kend)
-      st.consume(s_kv[s], s_kv[s] + TILE, jb * BS, rowpos, a.scale_log2, lane);
+    // 32 keys at a time; keys past the last block (stage rows loaded from
+    // the last block again) sit past every row's position and are masked.
+#pragma unroll
+    for (int kc = 0; kc < prefill_stage_keys<D>() / KC; ++kc) {
+      const int p0 = jb0 * BS + kc * KC;
+      if (p0 < nblk * BS && p0 < wave_kend)
+        st.consume(s_kv[s] + kc * KC * PITCH, s_kv[s] + SK + kc * KC * PITCH, p0, rowpos,
+                   a.scale_log2, lane);
+    }
     stage(s ^ 1);
     __syncthreads();
   }
