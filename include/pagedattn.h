@@ -204,10 +204,14 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * Sequences longer than one partition are split into partitions of
  * `partition_size` tokens (0 = library choice, see
  * pa_decode_partition_size); each partition's softmax state (max, sum,
- * unnormalised output) goes to the workspace and the last partition of that
- * (sequence, KV head) to finish -- found with an atomic arrival counter --
- * merges them with a log-sum-exp reduction in the same launch.  Results do
- * not depend on the order in which partitions finish (bit-identical reruns).
+ * unnormalised output) goes to the workspace and the partitions are merged
+ * with a log-sum-exp reduction.  With fewer than 16 partitions per sequence
+ * the last partition of that (sequence, KV head) to finish -- found with an
+ * atomic arrival counter -- merges them in the same launch; with 16 or more
+ * a second kernel, launched on the same stream, merges every split sequence
+ * (one long serial merge at the end of the first launch costs more than the
+ * launch).  Results do not depend on the order in which partitions finish
+ * (bit-identical reruns).
  *
  *   out            [num_seqs, num_q_heads, head_dim]                   (written)
  *   q              [num_seqs, num_q_heads, head_dim]                   (read)

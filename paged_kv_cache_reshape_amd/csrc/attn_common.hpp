@@ -35,6 +35,7 @@ struct DecodeArgs {
   int32_t part_blocks;   // partition kernel: blocks per partition
   int32_t max_parts;     // partition kernel: partitions per sequence, at most
   int32_t heads_per_wg;  // consecutive kv heads one workgroup takes (1, 2 or 4)
+  int32_t deferred_merge;  // 1: partitions store their states and a second kernel merges
   float scale_log2;      // scale * log2(e): scores are kept in base-2 units
 };
 
@@ -289,15 +290,15 @@ __device__ __forceinline__ void stream_blocks(int first, int step, int n, Fetch&
 //
 // The partial outputs are read with system-scope loads, which go to memory:
 // every thread first issues the loads of U pieces for all its output
-// elements, then folds them in, so that U * EPT loads are in flight per
-// thread instead of one round trip per value.
-template <class DT, int D, int GH, int NT, class RowFn>
+// elements, then folds them in, so that U * EPT (about kInFlight) loads are
+// in flight per thread instead of one round trip per value.
+template <class DT, int D, int GH, int NT, int kInFlight = 16, class RowFn>
 __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int npieces, int gh,
                                              RowFn piece_rows, size_t out_base,
                                              float (*s_pm)[GH], float (*s_pl)[GH]) {
   constexpr int kChunk = 64;
   constexpr int EPT = (GH * D + NT - 1) / NT;  // output elements per thread, at most
-  constexpr int U = EPT >= 16 ? 1 : 16 / EPT;  // pieces whose loads are issued together
+  constexpr int U = EPT >= kInFlight ? 1 : kInFlight / EPT;  // pieces loaded together
   const int tid = threadIdx.x;
   const int elems = gh * D;
   float rM[EPT], rL[EPT], rA[EPT];
@@ -491,14 +492,23 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
       store_out(DT{}, a.out, out_base + e, A / L);
     } else {
       const size_t pr = (((size_t)b * Hkv + gg * hpw + hwe) * a.max_parts + part) * G + hh;
-      publish(a.ws_acc + pr * D + d, A);
-      if (d == 0) {
-        publish(a.ws_ml + pr * 2 + 0, M);
-        publish(a.ws_ml + pr * 2 + 1, L);
+      if (a.deferred_merge) {
+        // Read by the merge kernel, after this launch has ended.
+        a.ws_acc[pr * D + d] = A;
+        if (d == 0) {
+          a.ws_ml[pr * 2 + 0] = M;
+          a.ws_ml[pr * 2 + 1] = L;
+        }
+      } else {
+        publish(a.ws_acc + pr * D + d, A);
+        if (d == 0) {
+          publish(a.ws_ml + pr * 2 + 0, M);
+          publish(a.ws_ml + pr * 2 + 1, L);
+        }
       }
     }
   }
-  if (nparts == 1) return;
+  if (nparts == 1 || a.deferred_merge) return;
 
   __shared__ int s_last;
   int32_t* counter = a.counters + (size_t)b * n_groups + gg;
@@ -518,6 +528,30 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
         out_base + (size_t)x * G * D, s_pm, s_pl);
   }
   reset_counter(counter);
+}
+
+// Body of the merge kernel that follows a partition launch with deferred
+// merge: one workgroup per (sequence, kv head) merges the partition states of
+// its G query heads into the output.  Sequences that fit one partition, and
+// empty or out-of-range contexts, were finished by the partition kernel.
+template <class DT, int D, int G, int NT>
+__device__ __forceinline__ void merge_partitions(const DecodeArgs& a, int bs) {
+  const int Hkv = a.num_kv_heads;
+  const int b = blockIdx.x / Hkv;
+  const int kvh = blockIdx.x % Hkv;
+  const int ctx = a.context_lens[b];
+  if (ctx <= 0 || ctx > a.max_blocks * bs) return;
+  const int part_tokens = a.part_blocks * bs;
+  const int nparts = (ctx + part_tokens - 1) / part_tokens;
+  if (nparts <= 1) return;
+  __shared__ float s_pm[64][G];
+  __shared__ float s_pl[64][G];
+  const size_t base = ((size_t)b * Hkv + kvh) * a.max_parts * G;
+  const size_t out_base = ((size_t)b * a.num_q_heads + (size_t)kvh * G) * D;
+  // Nothing else runs in this kernel: its registers take a whole chunk of
+  // pieces in one round trip.
+  merge_pieces<DT, D, G, NT, 64>(
+      a, nparts, G, [&](int p) { return base + (size_t)p * G; }, out_base, s_pm, s_pl);
 }
 
 }  // namespace pa

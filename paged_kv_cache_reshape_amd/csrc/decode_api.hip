@@ -60,6 +60,15 @@ bool use_mfma(int dtype, int D, int bs, int G) {
   return !(env && strcmp(env, "valu") == 0);
 }
 
+// Experimental: PAGEDATTN_MERGE=separate / inkernel forces where split
+// sequences are merged.
+bool deferred_merge(int max_parts) {
+  const char* env = getenv("PAGEDATTN_MERGE");
+  if (env && strcmp(env, "separate") == 0) return true;
+  if (env && strcmp(env, "inkernel") == 0) return false;
+  return max_parts >= 16;
+}
+
 struct Plan {
   int part_blocks;
   int max_parts;
@@ -168,7 +177,7 @@ extern "C" pa_status pa_paged_attention_decode(
   if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
                  block_size, partition_size, &plan)) {
     set_error("partition_size=%d must be 0 or a multiple of block_size=%d "
-              "between 1 and 64 blocks", partition_size, block_size);
+              "between 1 and 128 blocks", partition_size, block_size);
     return PA_ERR_INVALID_ARGUMENT;
   }
   if (plan.max_parts > 65535) {
@@ -223,6 +232,7 @@ extern "C" pa_status pa_paged_attention_decode(
   // The matrix-core kernel serves one kv head per workgroup (its eight waves
   // split the blocks).
   a.heads_per_wg = mfma ? 1 : plan.hpw;
+  a.deferred_merge = plan.max_parts > 1 && deferred_merge(plan.max_parts);
   a.scale_log2 = scale * 1.4426950408889634f;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -231,6 +241,13 @@ extern "C" pa_status pa_paged_attention_decode(
   if (err != hipSuccess) {
     set_error("decode launch failed: %s", hipGetErrorString(err));
     return PA_ERR_HIP;
+  }
+  if (a.deferred_merge) {
+    const hipError_t merr = launch_merge(dtype, head_dim, block_size, G, a, s);
+    if (merr != hipSuccess) {
+      set_error("merge launch failed: %s", hipGetErrorString(merr));
+      return PA_ERR_HIP;
+    }
   }
   return PA_OK;
 }

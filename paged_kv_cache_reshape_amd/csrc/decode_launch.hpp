@@ -47,5 +47,8 @@ hipError_t launch_partition(int dtype, int D, int BS, int G, const DecodeArgs& a
 bool mfma_supported(int dtype, int D, int BS, int G);
 hipError_t launch_mfma(int D, int BS, int G, const DecodeArgs& a, hipStream_t s);
 
+// Merge kernel run after a partition launch with deferred_merge set.
+hipError_t launch_merge(int dtype, int D, int BS, int G, const DecodeArgs& a, hipStream_t s);
+
 
 }  // namespace pa

@@ -76,11 +76,24 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
                                              s_m, s_l);
 }
 
+template <class DT, int D, int G, int NT>
+__global__ __launch_bounds__(NT) void merge_partitions_kernel(DecodeArgs a, int bs) {
+  merge_partitions<DT, D, G, NT>(a, bs);
+}
+
 template <class DT, int D, int BS, int G>
 hipError_t launch_partition_t(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.num_seqs * (a.num_kv_heads / a.heads_per_wg), a.max_parts);
   decode_partition_kernel<DT, D, BS, G, kDecodeWaves><<<grid, kDecodeWaves * 64, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+hipError_t launch_merge(int dtype, int D, int BS, int G, const DecodeArgs& a, hipStream_t s) {
+  return dispatch_decode(dtype, D, 16, G, [&](auto dt, auto d, auto, auto g) {
+    merge_partitions_kernel<decltype(dt), decltype(d)::value, decltype(g)::value, 256>
+        <<<a.num_seqs * a.num_kv_heads, 256, 0, s>>>(a, BS);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_partition(int dtype, int D, int BS, int G, const DecodeArgs& a,

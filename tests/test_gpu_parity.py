@@ -190,6 +190,23 @@ def test_decode_long_split_k_sampled():
     G.assert_close(out[seqs], ref, w.dtype, "long_splitk")
 
 
+@pytest.mark.parametrize("merge", ["inkernel", "separate"])
+@pytest.mark.parametrize("name,ps", [("f32_d128_bs32_g4", 64), ("bf16_d128_bs16_g16", 128),
+                                     ("bf16_d64_bs16_g2", 256), ("bf16_d64_bs32_g8", 64),
+                                     ("llama32_1b", 512)])
+def test_merge_paths_match_oracle(name, ps, merge, monkeypatch):
+    """Split sequences merged by the last partition workgroup to arrive, or by
+    the merge kernel that follows the partition launch."""
+    monkeypatch.setenv("PAGEDATTN_MERGE", merge)
+    inp = inputs_for(name)
+    w = inp["workload"]
+    say("write+decode", name, "partition", ps, "merge", merge)
+    d = G.upload(inp)
+    out = G.host_f64(gpu_step(d, ps))
+    ref, _ = oracle_step(inp)
+    G.assert_close(out, ref, w.dtype, f"{name} ps={ps} merge={merge}")
+
+
 @pytest.mark.parametrize("ps", [16, 64, 256, 1024, 1040, 2048])
 def test_partition_sizes_agree(ps):
     inp = inputs_for("qwen3_0p6b")
@@ -301,7 +318,7 @@ def test_nan_poison_bit_identical(name):
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("name,ps", [("qwen3_0p6b", 64), ("long_splitk", 512)])
+@pytest.mark.parametrize("name,ps", [("qwen3_0p6b", 64), ("qwen3_0p6b", 256), ("long_splitk", 512)])
 def test_rerun_bit_identical(name, ps):
     """P14: partitions finish in any order, the merge does not depend on it."""
     inp = inputs_for(name)
@@ -326,11 +343,14 @@ def test_empty_sequences_give_zero_rows():
     G.assert_close(out, ref, "bf16", "empty rows")
 
 
-def test_bad_table_entries_give_nan_rows_only():
+@pytest.mark.parametrize("merge", ["inkernel", "separate"])
+def test_bad_table_entries_give_nan_rows_only(merge, monkeypatch):
     """A block id outside the pool, or a length past the table, is never
-    dereferenced: that sequence's rows become NaN, the others are unchanged."""
+    dereferenced: that sequence's rows become NaN, the others are unchanged
+    (with split sequences merged in the partition kernel or after it)."""
+    monkeypatch.setenv("PAGEDATTN_MERGE", merge)
     inp = inputs_for("qwen3_0p6b")
-    say("decode bad table entries")
+    say("decode bad table entries, merge", merge)
     d = G.upload(inp)
     base = G.host_storage(gpu_step(d, 256))
     t = inp["block_tables"].copy()
@@ -364,9 +384,11 @@ def test_side_stream_and_given_out():
     assert np.array_equal(G.host_storage(out), base)
 
 
-def test_one_counter_array_serves_every_geometry():
+def test_one_counter_array_serves_every_geometry(monkeypatch):
     """Counters left at zero by each call: alternate two geometries whose
-    partial results overlap differently, with one shared counter array."""
+    partial results overlap differently, with one shared counter array
+    (merged in the partition kernel, the path that counts arrivals)."""
+    monkeypatch.setenv("PAGEDATTN_MERGE", "inkernel")
     cnt = torch.zeros(4096, dtype=torch.int32, device="cuda")
     cases = [("qwen3_0p6b", 64), ("bf16_d128_bs16_g16", 32), ("llama32_1b", 128),
              ("qwen3_0p6b", 32)]
@@ -443,20 +465,22 @@ def test_prefix_fork_copy_on_write():
 
 
 # ------------------------------------------------------------------ graph capture
-@pytest.mark.parametrize("name", ["qwen3_0p6b", "mqa_large"])
-def test_graph_replays_match_eager(name):
+@pytest.mark.parametrize("name,ps", [("qwen3_0p6b", None), ("mqa_large", None),
+                                     ("qwen3_0p6b", 64)])
+def test_graph_replays_match_eager(name, ps):
     """A step (KV write + decode) captured in a HIP graph: every replay, with
     eager launches and host synchronisations between replays, gives the eager
     result bit for bit.  The workspace and the arrival counters are allocated
     before capture and passed in, so nothing is allocated or cleared inside
-    the graph (the kernels leave the counters at zero themselves)."""
+    the graph (the kernels leave the counters at zero themselves).  At 64-token
+    partitions the step holds the separate merge kernel too."""
     inp = inputs_for(name)
     w = inp["workload"]
-    say("graph capture", name)
+    say("graph capture", name, ps)
     d = G.upload(inp)
     B, hq, hkv = w.num_seqs, w.num_q_heads, w.num_kv_heads
     mb = d["block_tables"].shape[1]
-    ps = w.partition_size
+    ps = w.partition_size if ps is None else ps
     ws = torch.empty(max(pa.decode_workspace_bytes(B, hq, hkv, w.head_dim, mb, w.block_size,
                                                    ps), 256), dtype=torch.uint8, device="cuda")
     cnt = torch.zeros(B * hkv, dtype=torch.int32, device="cuda")
