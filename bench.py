@@ -15,10 +15,14 @@ read, q read, output written, block-table entries, the write's rows) divided by
 the step time.  ``roofline`` is for the decode kernel alone: algorithmic bytes
 per launch over its mean launch time, from HIP events on the stream it runs on
 around K back-to-back launches.  ``graph_us_per_step`` is the same step
-replayed from a HIP graph.  ``prior_art`` times the pages' earlier design on
-the same GPU (gather the pages into dense tensors, then ordinary attention, in
-PyTorch).  ``cpu_baseline`` times the float64 CPU oracle on a bounded sample
-of the same batch.
+replayed from a HIP graph.  ``decode_us_loops`` / ``decode_us_median`` are
+five more loops of decode launches timed one by one; ``mall_resident`` is the
+decode reading one warm pool copy every launch; ``cache_line_efficiency`` is
+the decode's algorithmic bytes over the HBM bytes the counters measured (when
+they were taken on the current kernel sources).  ``prior_art`` times the
+pages' earlier design on the same GPU (gather the pages into dense tensors,
+then ordinary attention, in PyTorch).  ``cpu_baseline`` times the float64 CPU
+oracle on a bounded sample of the same batch, and again on one thread.
 """
 from __future__ import annotations
 
@@ -122,19 +126,27 @@ def gather_then_attention(q, k_cache, v_cache, block_tables, context_lens, scale
     return out.to(q.dtype), (k, v)
 
 
-def cpu_baseline(inp: dict, budget_s: float) -> dict:
-    """Time the float64 oracle's write + decode on a bounded sample."""
+def _one_thread():
+    """Context that holds the BLAS / OpenMP pools to one thread."""
+    from threadpoolctl import threadpool_limits
+    return threadpool_limits(limits=1)
+
+
+def _threads_used(cpu_s: float, wall_s: float) -> int:
+    """Threads a timed CPU region kept busy: process CPU time over wall time."""
+    return max(1, int(round(cpu_s / wall_s))) if wall_s > 0 else 1
+
+
+def _oracle_decode_sample(inp: dict, budget_s: float):
+    """The oracle's KV write, then its decode of the batch's sequences in
+    order until budget_s has passed.  Returns (KV bytes, sequences, wall s,
+    process CPU s)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
     w = inp["workload"]
     B = w.num_seqs
     done_bytes = 0
     seqs_done = 0
-    t0 = time.perf_counter()
+    t0, c0 = time.perf_counter(), time.process_time()
     k, v = oracle.reshape_and_cache(inp["key"], inp["value"], inp["k_cache"],
                                     inp["v_cache"], inp["slot_mapping"])
     b = 0
@@ -149,12 +161,25 @@ def cpu_baseline(inp: dict, budget_s: float) -> dict:
         b += 1
         if time.perf_counter() - t0 >= budget_s and seqs_done >= min(B, 4):
             break
-    dt = time.perf_counter() - t0
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s",
-            "cores": int(threads), "kind": "oracle",
+    return done_bytes, seqs_done, time.perf_counter() - t0, time.process_time() - c0
+
+
+def cpu_baseline(inp: dict, budget_s: float) -> dict:
+    """Time the float64 oracle's write + decode on a bounded sample, with the
+    host's thread pools as they are and again held to one thread.  `cores` is
+    the number of threads the run kept busy (CPU time over wall time): the
+    oracle's einsum contractions run on one thread either way."""
+    nb, ns, dt, cpu = _oracle_decode_sample(inp, budget_s)
+    with _one_thread():
+        nb1, ns1, dt1, _ = _oracle_decode_sample(inp, budget_s / 3)
+    return {"value": round(nb / dt / 1e9, 4), "unit": "GB/s",
+            "cores": _threads_used(cpu, dt), "kind": "oracle",
             "sample": (f"float64 numpy oracle: one full-pool KV write, then decode of "
-                       f"{seqs_done} sequences of this batch in order "
-                       f"({dt:.1f} s, {done_bytes / 1e6:.1f} MB of KV rows)")}
+                       f"{ns} sequences of this batch in order "
+                       f"({dt:.1f} s, {nb / 1e6:.1f} MB of KV rows)"),
+            "one_thread": {"value": round(nb1 / dt1 / 1e9, 4), "unit": "GB/s",
+                           "sample": f"same, {ns1} sequences with the thread pools held "
+                                     f"to one thread ({dt1:.1f} s)"}}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
@@ -171,14 +196,16 @@ def prefill_flops(inp: dict) -> int:
     return int(4 * w.num_q_heads * w.head_dim * keys)
 
 
-def prefill_cpu_baseline(inp: dict, budget_s: float) -> dict:
-    """Time the float64 oracle's prefill on the batch's first sequences."""
+def _oracle_prefill_sample(inp: dict, budget_s: float):
+    """The oracle's prefill of the batch's new tokens in order, one row at a
+    time, until budget_s has passed.  Returns (flops, rows, wall s, CPU s)."""
     import oracle
     w = inp["workload"]
     ctx, start = inp["context_lens"], inp["query_start"]
     k, v = oracle.reshape_and_cache(inp["key"], inp["value"], inp["k_cache"],
                                     inp["v_cache"], inp["slot_mapping"])
-    flops, rows, t0 = 0, 0, time.perf_counter()
+    flops, rows = 0, 0
+    t0, c0 = time.perf_counter(), time.process_time()
     for b in range(len(ctx)):
         lo, hi = int(start[b]), int(start[b + 1])
         for i in range(hi - lo):
@@ -192,16 +219,23 @@ def prefill_cpu_baseline(inp: dict, budget_s: float) -> dict:
                 break
         if time.perf_counter() - t0 >= budget_s:
             break
-    dt = time.perf_counter() - t0
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+    return flops, rows, time.perf_counter() - t0, time.process_time() - c0
+
+
+def prefill_cpu_baseline(inp: dict, budget_s: float) -> dict:
+    """Time the float64 oracle's prefill on the batch's first new tokens, with
+    the thread pools as they are and held to one thread; `cores` as in
+    cpu_baseline."""
+    fl, rows, dt, cpu = _oracle_prefill_sample(inp, budget_s)
+    with _one_thread():
+        fl1, rows1, dt1, _ = _oracle_prefill_sample(inp, budget_s / 3)
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": _threads_used(cpu, dt), "kind": "oracle",
             "sample": f"float64 numpy oracle prefill, the first {rows} new tokens of the "
-                      f"batch in order ({dt:.1f} s)"}
+                      f"batch in order ({dt:.1f} s)",
+            "one_thread": {"value": round(fl1 / dt1 / 1e12, 6), "unit": "TFLOP/s",
+                           "sample": f"same, the first {rows1} new tokens with the thread "
+                                     f"pools held to one thread ({dt1:.1f} s)"}}
 
 
 def run_prefill(args, torch, pa) -> int:
@@ -403,6 +437,17 @@ def main() -> int:
     # between launches, so the figures compare with a kernel trace).
     k_mean_s = timed(decode, args.steps, args.warmup + args.steps) / 1e3
     w_mean_s = timed(write, args.steps, args.warmup) / 1e3
+    # Spread: five more loops of decode launches, each timed on its own.
+    n_loop = max(20, args.steps // 5)
+    loops_us = [timed(decode, n_loop, j * n_loop) * 1e3 for j in range(5)]
+    # Warm single pool: every launch reads the same pool copy, which the
+    # 256 MB last-level cache can hold when the pool is smaller than it.
+    def decode_one_pool(i):
+        pa.paged_attention_decode(q, kc0, vc0, tables, lens, scale, partition_size=ps,
+                                  out=out, workspace=ws, counters=counters)
+    for i in range(3):
+        decode_one_pool(i)
+    warm_s = timed(decode_one_pool, args.steps, 0) / 1e3
 
     # The same steps replayed from a HIP graph (one graph holds one step per
     # pool copy); buffers were all allocated above, so capture allocates nothing.
@@ -473,6 +518,17 @@ def main() -> int:
         "decode_us_mean": round(k_mean_s * 1e6, 3),
         "write_us_mean": round(w_mean_s * 1e6, 3),
         "decode_kv_gbs": round(nbytes["kv"] / k_mean_s / 1e9, 3),
+        "decode_us_loops": [round(x, 3) for x in loops_us],
+        "decode_us_median": round(float(np.median(loops_us)), 3),
+        "mall_resident": {
+            "decode_us_mean": round(warm_s * 1e6, 3),
+            "decode_gbs": round(nbytes["decode"] / warm_s / 1e9, 3),
+            "pool_bytes": int(pool_bytes),
+            "note": "one pool copy read by every launch (warm caches), not HBM-bound "
+                    "when the pool fits the 256 MB last-level cache",
+        },
+        "cache_line_efficiency": (None if not traffic
+                                  else round(nbytes["decode"] / traffic, 4)),
         "graph_us_per_step": None if graph_us is None else round(graph_us, 3),
         "roofline": {
             "bound": "hbm",
