@@ -34,11 +34,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   using Sh = TileShape<D, BS, G>;
   using T = RowTileAttn<D, BS, G>;
   constexpr int RL = Sh::RL, ROWS = Sh::ROWS, NI = Sh::NI;
-  constexpr int PITCH = Sh::PITCH, TILE = Sh::TILE;
+  constexpr int KPITCH = Sh::KPITCH, VPITCH = Sh::VPITCH;
+  constexpr int KTILE = Sh::KTILE, VTILE = Sh::VTILE;
   constexpr int NT = NW * 64;
   // LDS: per wave a K and a V tile while streaming; afterwards the same bytes
   // hold the waves' states for the combine.
-  constexpr int kStage = NW * 2 * TILE;
+  constexpr int kStage = NW * (KTILE + VTILE);
   constexpr int kCombine = NW * G * (D + 2) * 4;
   __shared__ __attribute__((aligned(16))) char s_raw[kStage > kCombine ? kStage : kCombine];
 
@@ -52,11 +53,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   const int tw = wave / hpw;
 
   T st;
+  const QScale qs(a.scale_log2);
   PartitionWork w;
   if (!partition_prologue<BF16, D, BS, G, NT>(a, lane, w, [&](int b, int gg) {
         const uint16_t* q_grp = static_cast<const uint16_t*>(a.q) +
                                 ((size_t)b * a.num_q_heads + (size_t)(gg * hpw + hw) * G) * D;
-        st.load_q([&](int h) { return h < G ? q_grp + (size_t)h * D : nullptr; }, lane);
+        st.load_q([&](int h) { return h < G ? q_grp + (size_t)h * D : nullptr; }, qs, lane);
       }))
     return;
   const int g = w.gg * hpw + hw;
@@ -91,16 +93,16 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     for (int i = 0; i < NI; ++i)
       vr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off[i], 0, 0));
   };
-  char* kt = s_raw + wave * 2 * TILE;
-  char* vt = kt + TILE;
+  char* kt = s_raw + wave * (KTILE + VTILE);
+  char* vt = kt + KTILE;
   auto consume = [&](int jb, bool live, const uint4 (&kr)[NI], const uint4 (&vr)[NI]) {
     // Stage the block (this wave's tile only; LDS keeps one wave's accesses
     // in order, so the reads below see these writes).
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int tok = i * ROWS + row;
-      *reinterpret_cast<uint4*>(kt + tok * PITCH + col * 16) = kr[i];
-      *reinterpret_cast<uint4*>(vt + tok * PITCH + col * 16) = vr[i];
+      *reinterpret_cast<uint4*>(kt + tok * KPITCH + col * 16) = kr[i];
+      *reinterpret_cast<uint4*>(vt + tok * VPITCH + col * 16) = vr[i];
     }
     __builtin_amdgcn_wave_barrier();
     // Every existing row sits at the newest position; masked when not live.
@@ -108,7 +110,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int ht = 0; ht < T::HT; ++ht)
       rowpos[ht] = live && 16 * ht + (lane & 15) < G ? w.ctx - 1 : -1;
-    st.consume(kt, vt, (w.blk0 + jb) * BS, rowpos, a.scale_log2, lane);
+    // Only the sequence's last block holds keys past the newest position.
+    const int pos0 = (w.blk0 + jb) * BS;
+    st.consume(kt, vt, pos0, rowpos, !live || pos0 + BS > w.ctx, qs.c, lane);
     __builtin_amdgcn_wave_barrier();
   };
   stream_blocks<NI, kGroupPrefetch>(tw, nwt, w.nblk_run, fetch, consume);

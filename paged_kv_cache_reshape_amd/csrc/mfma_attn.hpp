@@ -11,7 +11,11 @@
 //     against token 4j + r of the 16-token tile;
 //   * each score is kept when its key position is at most the row's own
 //     position (the decode's rows all sit at the last position; prefill rows
-//     are causal), else it becomes -inf;
+//     are causal), else it becomes -inf -- only in tiles where some key can
+//     lie past some row (the caller says which), the others skip the test;
+//   * the scale is applied inside the exponent, p = exp2(c s - m), one fused
+//     multiply-add per score, with c > 0: a negative scale is carried by
+//     negating q (exact in bf16) and a zero scale by zeroing q, c = 1;
 //   * online softmax per row in that layout (block maximum by two lane swaps),
 //     with a lazy maximum: the kept maximum moves only when a score of the
 //     block passes it by more than 8 (base 2), so every weight is at most 256
@@ -22,10 +26,11 @@
 //   * O += P V with the same MFMA: C of the first product is already laid out
 //     as the A operand (lane (j, n): row n, tokens 4j .. 4j+3); V arrives
 //     transposed from LDS through ds_read_b64_tr_b16, which gives lane (j, n)
-//     the values of tokens 4j .. 4j+3 at one d.  P is split as
-//     bf16(p) + bf16(p - bf16(p)), two products, so the weights keep 16
-//     significant bits (one bf16 rounding of p costs up to 2^-9 relative per
-//     weight, more than the output tolerance allows).
+//     the values of tokens 4j .. 4j+3 at one d.  P is split as hi + bf16(lo),
+//     hi = p with its low 16 bits cleared (a bf16 value), lo = p - hi (exact),
+//     two products, so the weights keep 16 significant bits (one bf16
+//     rounding of p costs up to 2^-9 relative per weight, more than the output
+//     tolerance allows).
 #pragma once
 
 #include "attn_common.hpp"
@@ -35,6 +40,15 @@ namespace pa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to bfloat16 (nearest even), packed low-first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = __builtin_convertvector((f32x2){a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer resource word 3 for gfx9-family raw buffer loads (32-bit data
@@ -50,8 +64,37 @@ struct TileShape {
   static constexpr int HT = (NR + 15) / 16; // 16-row tiles of query rows
   static constexpr int DK = D / 32;         // 32-wide d chunks of q.k
   static constexpr int DT = D / 16;         // 16-wide d tiles of p.v
-  static constexpr int PITCH = D * 2 + 16;  // LDS row pitch, bytes (padding spreads banks)
-  static constexpr int TILE = BS * PITCH;   // one of K or V for one block
+  // LDS row pitches, bytes, chosen so that neither read pattern meets a bank
+  // conflict (64 banks of 4 bytes): K rows are read 16 bytes a lane, 16 rows
+  // at a time, so rows step 4 banks (+16 bytes); V rows are read 8 bytes a
+  // lane, 4 lanes a row, 8 rows at a time, so rows step 8 banks (+32 bytes).
+  static constexpr int KPITCH = D * 2 + 16;
+  static constexpr int VPITCH = D * 2 + 32;
+  static constexpr int KTILE = BS * KPITCH;  // K rows of one block
+  static constexpr int VTILE = BS * VPITCH;  // V rows of one block
+};
+
+// How the query rows carry the softmax scale.  Scores are used as
+// exp2(c * (q.k) - m) with c > 0; scale * log2(e) = c * sign, where the sign
+// (-1 or 0) is applied to q as it is loaded: negating a bf16 value, or
+// zeroing it, is exact.  A NaN scale stays in c (every output NaN).
+struct QScale {
+  float c;
+  uint32_t mask;  // applied to q's bits: and-mask, then xor with flip
+  uint32_t flip;
+  __device__ __forceinline__ explicit QScale(float scale_log2) {
+    if (scale_log2 < 0.0f) {
+      c = -scale_log2; mask = 0xFFFFFFFFu; flip = 0x80008000u;
+    } else if (scale_log2 == 0.0f) {
+      c = 1.0f; mask = 0u; flip = 0u;
+    } else {
+      c = scale_log2; mask = 0xFFFFFFFFu; flip = 0u;
+    }
+  }
+  __device__ __forceinline__ uint4 apply(uint4 v) const {
+    return make_uint4((v.x & mask) ^ flip, (v.y & mask) ^ flip, (v.z & mask) ^ flip,
+                      (v.w & mask) ^ flip);
+  }
 };
 
 __device__ __forceinline__ float max4(f32x4 v) {
@@ -63,7 +106,6 @@ template <int D, int BS, int NR>
 struct RowTileAttn {
   using Sh = TileShape<D, BS, NR>;
   static constexpr int TPB = Sh::TPB, HT = Sh::HT, DK = Sh::DK, DT = Sh::DT;
-  static constexpr int PITCH = Sh::PITCH;
   static constexpr float kLazy = 8.0f;
 
   bf16x8 qb[HT][DK];  // B operand of q.k: lane (j, n) holds row 16 ht + n, d = 32 i + 8 j ..
@@ -82,16 +124,17 @@ struct RowTileAttn {
   }
 
   // row_ptr(r): element pointer to query row r (D values), or nullptr for a
-  // row that does not exist (it is then zero and every score of it masked).
+  // row that does not exist (it is then zero: its scores are finite and its
+  // output is never stored).  The rows are taken with qs's sign.
   template <class RowPtr>
-  __device__ __forceinline__ void load_q(RowPtr&& row_ptr, int lane) {
+  __device__ __forceinline__ void load_q(RowPtr&& row_ptr, const QScale& qs, int lane) {
     const int n = lane & 15, j = lane >> 4;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       const uint16_t* p = row_ptr(16 * ht + n);
 #pragma unroll
       for (int i = 0; i < DK; ++i) {
-        const uint4 v = p ? load_chunk(p + 32 * i + 8 * j) : make_uint4(0, 0, 0, 0);
+        const uint4 v = p ? qs.apply(load_chunk(p + 32 * i + 8 * j)) : make_uint4(0, 0, 0, 0);
         qb[ht][i] = __builtin_bit_cast(bf16x8, v);
       }
     }
@@ -116,56 +159,88 @@ struct RowTileAttn {
       for (int r = 0; r < 4; ++r) o[ht][dt][r] *= f[r];
   }
 
-  // One block, staged in LDS at kt / vt (rows of PITCH bytes, token-major,
-  // every row finite).  pos0: sequence position of the block's first token;
-  // rowpos[ht]: this lane's row position (lane (j, n) -> row 16 ht + n);
-  // keys past a row's position are masked (a row position of -1 masks all).
+  // One block, staged in LDS at kt (K rows, KPITCH bytes apart) and vt (V
+  // rows, VPITCH apart), token-major, every row finite.  pos0: sequence
+  // position of the block's first token; rowpos[ht]: this lane's row
+  // position (lane (j, n) -> row 16 ht + n).  With `masked` (uniform), keys
+  // past a row's position are masked (a row position of -1 masks all);
+  // without it every key is taken, so the caller clears it only for blocks
+  // that lie wholly at or before every live row's position.  c: QScale::c.
   // All scores of the block are formed first, so that one kept maximum per
   // row serves every weight of the block.
   __device__ __forceinline__ void consume(const char* kt, const char* vt, int pos0,
-                                          const int (&rowpos)[HT], float scale_log2, int lane) {
+                                          const int (&rowpos)[HT], bool masked, float c,
+                                          int lane) {
     const int n = lane & 15, j = lane >> 4;
-    f32x4 x[HT][TPB];
+    f32x4 x[HT][TPB];  // raw scores q.k (-inf where masked)
 #pragma unroll
     for (int tt = 0; tt < TPB; ++tt) {
       bf16x8 ka[DK];
 #pragma unroll
       for (int i = 0; i < DK; ++i)
-        ka[i] = *reinterpret_cast<const bf16x8*>(kt + (tt * 16 + n) * PITCH + (32 * i + 8 * j) * 2);
-      const int kp = pos0 + tt * 16 + 4 * j;  // key position of register 0
+        ka[i] = *reinterpret_cast<const bf16x8*>(kt + (tt * 16 + n) * Sh::KPITCH +
+                                                 (32 * i + 8 * j) * 2);
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < DK; ++i)
           s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i], qb[ht][i], s, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          x[ht][tt][r] = kp + r <= rowpos[ht] ? s[r] * scale_log2 : -INFINITY;
+        x[ht][tt] = s;
       }
     }
-    bf16x4 ph[HT][TPB], pl[HT][TPB];
+    if (masked) {
+#pragma unroll
+      for (int tt = 0; tt < TPB; ++tt) {
+        const int kp = pos0 + tt * 16 + 4 * j;  // key position of register 0
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            x[ht][tt][r] = kp + r <= rowpos[ht] ? x[ht][tt][r] : -INFINITY;
+      }
+    }
+    // Weights as p.v's A operand, one bf16x8 per pair of 16-token tiles
+    // (lane (j, n): row n, tokens 4j .. 4j+3 of each tile of the pair).
+    constexpr int NP = TPB >= 2 ? TPB / 2 : 1;
+    bf16x8 ph[HT][NP], pl[HT][NP];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       float bmax = max4(x[ht][0]);
 #pragma unroll
       for (int tt = 1; tt < TPB; ++tt) bmax = fmaxf(bmax, max4(x[ht][tt]));
       bmax = fmaxf(bmax, lane_xor<16>(bmax));
-      bmax = fmaxf(bmax, lane_xor<32>(bmax));
+      bmax = fmaxf(bmax, lane_xor<32>(bmax)) * c;  // c > 0: the scaled maximum
       if (__builtin_amdgcn_ballot_w64(bmax > mth[ht]) != 0)
         rescale(ht, fmaxf(m[ht], bmax), lane);
       float sum = 0.0f;
+      uint32_t hw[TPB * 2], lw[TPB * 2];
 #pragma unroll
       for (int tt = 0; tt < TPB; ++tt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(x[ht][tt][r] - m[ht]);
-          sum += p;
-          const __bf16 hi = static_cast<__bf16>(p);
-          ph[ht][tt][r] = hi;
-          pl[ht][tt][r] = static_cast<__bf16>(p - static_cast<float>(hi));
+        for (int r = 0; r < 4; r += 2) {
+          const float p0 = fast_exp2(fmaf(x[ht][tt][r], c, -m[ht]));
+          const float p1 = fast_exp2(fmaf(x[ht][tt][r + 1], c, -m[ht]));
+          sum += p0 + p1;
+          const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
+          hw[tt * 2 + r / 2] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // high halves
+          const float l0 = p0 - __uint_as_float(b0 & 0xFFFF0000u);
+          const float l1 = p1 - __uint_as_float(b1 & 0xFFFF0000u);
+          lw[tt * 2 + r / 2] = pack_bf16x2(l0, l1);
         }
       l[ht] += sum;
+      if constexpr (TPB >= 2) {
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+          ph[ht][pp] = __builtin_bit_cast(
+              bf16x8, make_uint4(hw[4 * pp], hw[4 * pp + 1], hw[4 * pp + 2], hw[4 * pp + 3]));
+          pl[ht][pp] = __builtin_bit_cast(
+              bf16x8, make_uint4(lw[4 * pp], lw[4 * pp + 1], lw[4 * pp + 2], lw[4 * pp + 3]));
+        }
+      } else {
+        ph[ht][0] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], 0u, 0u));
+        pl[ht][0] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], 0u, 0u));
+      }
     }
     // O += P V, one 16-wide d tile at a time; V arrives transposed from LDS.
     const int L = lane & 15;
@@ -174,25 +249,32 @@ struct RowTileAttn {
       bf16x4 vb[TPB];
 #pragma unroll
       for (int tt = 0; tt < TPB; ++tt) {
-        const char* p = vt + (tt * 16 + 4 * j + (L >> 2)) * PITCH + (16 * dt + 4 * (L & 3)) * 2;
+        const char* p =
+            vt + (tt * 16 + 4 * j + (L >> 2)) * Sh::VPITCH + (16 * dt + 4 * (L & 3)) * 2;
         vb[tt] = __builtin_bit_cast(
             bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (__attribute__((address_space(3))) s16x4*)(p)));
       }
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        if constexpr (TPB == 2) {
-          const bf16x8 b = __builtin_shufflevector(vb[0], vb[1], 0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8 ah = __builtin_shufflevector(ph[ht][0], ph[ht][1], 0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8 al = __builtin_shufflevector(pl[ht][0], pl[ht][1], 0, 1, 2, 3, 4, 5, 6, 7);
-          o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, o[ht][dt], 0, 0, 0);
-          o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, o[ht][dt], 0, 0, 0);
+        if constexpr (TPB >= 2) {
+#pragma unroll
+          for (int pp = 0; pp < NP; ++pp) {
+            const bf16x8 b =
+                __builtin_shufflevector(vb[2 * pp], vb[2 * pp + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+            o[ht][dt] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[ht][pp], b, o[ht][dt], 0, 0, 0);
+            o[ht][dt] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[ht][pp], b, o[ht][dt], 0, 0, 0);
+          }
         } else {
           const s16x4 b = __builtin_bit_cast(s16x4, vb[0]);
-          o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              __builtin_bit_cast(s16x4, ph[ht][0]), b, o[ht][dt], 0, 0, 0);
-          o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              __builtin_bit_cast(s16x4, pl[ht][0]), b, o[ht][dt], 0, 0, 0);
+          const s16x8 h8 = __builtin_bit_cast(s16x8, ph[ht][0]);
+          const s16x8 l8 = __builtin_bit_cast(s16x8, pl[ht][0]);
+          const s16x4 ah = __builtin_shufflevector(h8, h8, 0, 1, 2, 3);
+          const s16x4 al = __builtin_shufflevector(l8, l8, 0, 1, 2, 3);
+          o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, b, o[ht][dt], 0, 0, 0);
+          o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, b, o[ht][dt], 0, 0, 0);
         }
       }
     }

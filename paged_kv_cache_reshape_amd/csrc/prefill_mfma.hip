@@ -11,9 +11,12 @@
 //
 // Query rows are (token, head) pairs: row r of sequence b is new token r / G,
 // query head g * G + r % G of kv head g.  A workgroup takes 8 waves x 32 rows
-// of one (sequence, kv head); rows of later tokens see more keys, so the
-// grid's row groups are issued last-first.  Per K/V block (the blocks up to
-// the workgroup's last row position):
+// (a row group) of one (sequence, kv head).  Row groups differ in cost -- the
+// keys they fold, up to their last row's position -- so the workgroups take
+// them longest first (pick_unit: the grid is ranked, not laid out by
+// sequence; a hardware dispatcher that hands workgroups out in order would
+// otherwise leave compute units idle behind long ones).  Per K/V block (the
+// blocks up to the workgroup's last row position):
 //   * the whole workgroup loads 64 keys' worth of blocks (K and V rows for kv
 //     head g) with full-row coalesced 16-byte loads into one of two LDS stages
 //     (the next stage's loads are in flight while the current one is used);
@@ -27,6 +30,8 @@
 #include "decode_launch.hpp"
 
 #include <stdlib.h>
+
+#include <algorithm>
 
 namespace pa {
 
@@ -42,41 +47,181 @@ struct PrefillArgs {
   int32_t num_kv_heads;
   int32_t num_blocks;
   int32_t max_blocks;
-  int32_t row_groups;  // workgroups per (sequence, kv head) along the query rows
+  int32_t num_seqs;
+  int32_t row_groups;    // row groups of the longest sequence (grid: num_seqs x this)
+  int32_t bucket_width;  // keys per cost bucket of the longest-first order
+  int32_t num_buckets;   // cost buckets, at most kMaxCostBuckets
   float scale_log2;
 };
 
-constexpr int kPrefillWaves = 8;
+constexpr int kMaxCostBuckets = 1024;
+
+// The row group a workgroup takes.  Units are (sequence b, row group rg); a
+// unit folds first_b + min(n_b, (rg + 1) T) keys (first_b = cached positions
+// before the new tokens, n_b new tokens, T tokens per row group).  Units are
+// ranked by that cost in buckets of bucket_width keys, highest first, then by
+// b ascending and rg descending; workgroup `u` (of each kv head) takes the
+// unit of rank u.  Every workgroup of the launch computes the same ranking
+// from the lengths: a histogram of unit costs, its suffix sums, then the
+// unit within the bucket by a scan over the sequences.  Returns false (in
+// every thread) when u is past the last unit.
+template <int G, int RPW, int NT>
+__device__ __forceinline__ bool pick_unit(const PrefillArgs& a, int max_tokens, int u,
+                                          int& b_out, int& rg_out) {
+  constexpr int T = RPW / G;  // tokens per row group
+  __shared__ int s_hist[kMaxCostBuckets];
+  __shared__ int s_cum[kMaxCostBuckets];
+  __shared__ int s_wsum[NT / 64];
+  __shared__ int s_pick[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int B = a.num_seqs, W = a.bucket_width, NBK = a.num_buckets;
+  auto seq = [&](int bb, int& first, int& n) {
+    const int q0 = a.query_start[bb];
+    n = a.query_start[bb + 1] - q0;
+    const int c = a.context_lens[bb];
+    const bool ok = n >= 0 && n <= c && c <= max_tokens;
+    first = ok ? c - n : 0;
+    n = n < 0 ? 0 : n;
+  };
+  auto groups = [&](int n) { return (int)(((int64_t)n * G + RPW - 1) / RPW); };
+  auto bucket = [&](int first, int n, int rg) {
+    const int cost = first + min(n, (rg + 1) * T);
+    return min(max((cost - 1) / W, 0), NBK - 1);
+  };
+  // Wave-wide inclusive prefix sum.
+  auto wave_scan = [&](int v) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(v, d);
+      v += lane >= d ? o : 0;
+    }
+    return v;
+  };
+
+  for (int k = tid; k < NBK; k += NT) s_hist[k] = 0;
+  __syncthreads();
+  for (int bb = tid; bb < B; bb += NT) {
+    int first, n;
+    seq(bb, first, n);
+    const int ng = groups(n);
+    for (int rg = 0; rg < ng; ++rg) atomicAdd(&s_hist[bucket(first, n, rg)], 1);
+  }
+  __syncthreads();
+  if (wave == 0) {  // s_cum[k] = units in buckets above k; lane 0 takes the top ones
+    const int per = (NBK + 63) / 64;
+    const int top = NBK - 1 - lane * per;
+    int sum = 0;
+    for (int i = 0; i < per; ++i)
+      if (top - i >= 0) sum += s_hist[top - i];
+    const int incl = wave_scan(sum);
+    int run = incl - sum;
+    for (int i = 0; i < per; ++i)
+      if (top - i >= 0) {
+        s_cum[top - i] = run;
+        run += s_hist[top - i];
+      }
+    if (lane == 63) s_pick[2] = incl;  // all units
+  }
+  __syncthreads();
+  if (u >= s_pick[2]) return false;
+  for (int k = tid; k < NBK; k += NT)
+    if (s_hist[k] > 0 && s_cum[k] <= u && u < s_cum[k] + s_hist[k]) {
+      s_pick[0] = k;
+      s_pick[1] = u - s_cum[k];
+    }
+  __syncthreads();
+  const int kstar = s_pick[0], r = s_pick[1];
+  // Units in bucket kstar, sequences in order: each thread takes a range of
+  // sequences, counts theirs, and a scan over the threads finds the one.
+  const int per_b = (B + NT - 1) / NT;
+  const int b_lo = min(B, tid * per_b), b_hi = min(B, b_lo + per_b);
+  auto count_in = [&](int bb) {
+    int first, n;
+    seq(bb, first, n);
+    int c = 0;
+    for (int rg = groups(n) - 1; rg >= 0; --rg) c += bucket(first, n, rg) == kstar;
+    return c;
+  };
+  int cnt = 0;
+  for (int bb = b_lo; bb < b_hi; ++bb) cnt += count_in(bb);
+  const int incl = wave_scan(cnt);
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int pre = incl - cnt;
+  for (int w = 0; w < wave; ++w) pre += s_wsum[w];
+  if (r >= pre && r < pre + cnt) {
+    for (int bb = b_lo; bb < b_hi; ++bb) {
+      int first, n;
+      seq(bb, first, n);
+      for (int rg = groups(n) - 1; rg >= 0; --rg)
+        if (bucket(first, n, rg) == kstar) {
+          if (pre == r) {
+            s_pick[0] = bb;
+            s_pick[1] = rg;
+          }
+          ++pre;
+        }
+    }
+  }
+  __syncthreads();
+  b_out = s_pick[0];
+  rg_out = s_pick[1];
+  return true;
+}
+
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 8
+#endif
+#ifndef PA_PREFILL_STAGE_KEYS
+#define PA_PREFILL_STAGE_KEYS 64
+#endif
+#ifndef PA_PREFILL_FOLD_KEYS
+#define PA_PREFILL_FOLD_KEYS 64
+#endif
+#ifndef PA_PREFILL_DEPTH
+#define PA_PREFILL_DEPTH 2
+#endif
+constexpr int kPrefillWaves = PA_PREFILL_WAVES;
+constexpr int kPrefillDepth = PA_PREFILL_DEPTH;  // stages of K/V loads in flight (1 or 2)
 constexpr int kPrefillRows = 32;  // query rows per wave
 // Keys per LDS stage (several blocks): 64, or 32 at head_dim 64, where the
 // workgroup is held to 128 VGPRs so that two fit on a compute unit.
 template <int D>
-constexpr int prefill_stage_keys() { return D == 64 ? 32 : 64; }
+constexpr int prefill_stage_keys() { return D == 64 ? 32 : PA_PREFILL_STAGE_KEYS; }
 
 template <int D, int BS, int G, int NW>
 __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int NR = kPrefillRows;
-  constexpr int KC = 32;  // keys folded per call: two 16-token tiles, so p.v runs on
-                          // v_mfma_f32_16x16x32_bf16 whatever the block size
+  // Keys folded per call: a whole stage (two or four 16-token tiles, so p.v
+  // runs on v_mfma_f32_16x16x32_bf16 whatever the block size); one running
+  // maximum update and one branch per call.
+  constexpr int KC = PA_PREFILL_FOLD_KEYS < prefill_stage_keys<D>() ? PA_PREFILL_FOLD_KEYS
+                                                                     : prefill_stage_keys<D>();
   using Sh = TileShape<D, KC, NR>;
   using T = RowTileAttn<D, KC, NR>;
-  constexpr int RL = Sh::RL, PITCH = Sh::PITCH, HT = Sh::HT;
+  constexpr int RL = Sh::RL, KPITCH = Sh::KPITCH, VPITCH = Sh::VPITCH, HT = Sh::HT;
   constexpr int NT = NW * 64;
   constexpr int kChunks = BS * RL;  // 16-byte chunks of one block's rows, K or V
   static_assert(kChunks % 64 == 0, "a wave's chunks are all K or all V");
   constexpr int NCH = (2 * kChunks + NT - 1) / NT;  // chunks per thread per block, K and V
   constexpr int KB = prefill_stage_keys<D>() / BS;              // blocks per stage
-  constexpr int SK = prefill_stage_keys<D>() * PITCH;           // one stage's K (or V) rows
+  constexpr int SK = prefill_stage_keys<D>() * KPITCH;          // one stage's K rows
+  constexpr int SV = prefill_stage_keys<D>() * VPITCH;          // one stage's V rows
   // [stage][K rows | V rows]: the stage's KB blocks are consecutive logical
   // blocks, so row t of a stage is key position (first block) * BS + t.
-  __shared__ __attribute__((aligned(16))) char s_kv[2][2 * SK];
+  __shared__ __attribute__((aligned(16))) char s_kv[2][SK + SV];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
-  const int b = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
-  const int rg = a.row_groups - 1 - (int)blockIdx.y;  // later rows first
+  // Workgroup L takes kv head L % Hkv (so, with Hkv a multiple of the eight
+  // XCDs that workgroups are dealt to in turn, a head's K/V stays in one
+  // XCD's L2) of the unit ranked L / Hkv.
+  const int L = blockIdx.y * gridDim.x + blockIdx.x;
+  const int g = L % Hkv;
+  int b, rg;
+  if (!pick_unit<G, NW * NR, NT>(a, a.max_blocks * BS, L / Hkv, b, rg)) return;
   const int qs = a.query_start[b];
   const int nq = a.query_start[b + 1] - qs;
   const int ctx = a.context_lens[b];
@@ -99,6 +244,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(
   const int wr0 = r0 + wave * NR;  // this wave's first row
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   T st;
+  const QScale qsc(a.scale_log2);
   st.reset();
   st.load_q(
       [&](int r) -> const uint16_t* {
@@ -106,15 +252,17 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(
         return R < nrows ? q + ((size_t)(qs + R / G) * Hq + (size_t)g * G + R % G) * D
                          : nullptr;
       },
-      lane);
+      qsc, lane);
   int rowpos[HT];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
     const int R = wr0 + 16 * ht + (lane & 15);
     rowpos[ht] = R < nrows ? first + R / G : -1;
   }
-  // Keys this wave's rows reach (0 if it has no rows).
+  // Keys this wave's rows reach (0 if it has no rows); chunks ending at or
+  // before its first row's position need no causal mask.
   const int wave_kend = wr0 < nrows ? first + (min(nrows, wr0 + NR) - 1) / G + 1 : 0;
+  const int wave_pos0 = first + wr0 / G;
 
   // Block loads: chunk c < 2 * kChunks is K chunk c or V chunk c - kChunks;
   // chunk cc of a block is token cc / RL, 16 bytes at d = 8 (cc % RL).  Every
@@ -127,15 +275,18 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(
   const uint32_t head_off = (uint32_t)g * D * 2;
   const char* kbase = static_cast<const char*>(a.k_cache);
   const char* vbase = static_cast<const char*>(a.v_cache);
-  const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks;
+  // The table row is read through the constant address space: scalar loads,
+  // counted apart from the vector loads, so fetching a stage's entries never
+  // waits for the K/V loads still in flight (vector loads complete in order).
+  const __attribute__((address_space(4))) int32_t* trow =
+      (const __attribute__((address_space(4))) int32_t*)(a.block_tables +
+                                                          (size_t)b * a.max_blocks);
   bool bad = false;  // a block id outside the pool: rows become NaN
-  uint4 r[KB][NCH];
+  uint4 r[kPrefillDepth][KB][NCH];  // stages of K/V rows in flight
   auto chunk = [&](int i) { return (tid + i * NT) % (2 * kChunks); };
-  // Loads of blocks jb0 .. jb0 + KB - 1 (ids past the last block read the last
-  // one again: in range, never folded in).
-  auto fetch = [&](int jb0) {
-    // Table entries first, all together: a vector load completes in order,
-    // so waiting for an entry between K/V loads would wait for those too.
+  // Loads of blocks jb0 .. jb0 + KB - 1 into register set rs (ids past the
+  // last block read the last one again: in range, never folded in).
+  auto fetch = [&](uint4 (&rr)[KB][NCH], int jb0) {
     int ids[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) ids[kb] = trow[jb0 + kb < nblk ? jb0 + kb : nblk - 1];
@@ -162,12 +313,12 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(
         // Tokens at or past the context read the block's token 0 (finite).
         const uint32_t off = head_off + 16u * (cc % RL) +
                              (pos0 + tok < ctx ? (uint32_t)tok * tok_bytes : 0u);
-        r[kb][i] = __builtin_bit_cast(
+        rr[kb][i] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(is_k ? rk : rv, off, 0, 0));
       }
     }
   };
-  auto stage = [&](int s) {
+  auto stage = [&](const uint4 (&rr)[KB][NCH], int s) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -175,32 +326,60 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(
         const int c = chunk(i);
         const bool is_k = __builtin_amdgcn_readfirstlane(c) < kChunks;
         const int cc = is_k ? c : c - kChunks;
-        *reinterpret_cast<uint4*>(s_kv[s] + (is_k ? 0 : SK) + (kb * BS + cc / RL) * PITCH +
-                                  (cc % RL) * 16) = r[kb][i];
+        *reinterpret_cast<uint4*>(s_kv[s] + (is_k ? (kb * BS + cc / RL) * KPITCH
+                                                  : SK + (kb * BS + cc / RL) * VPITCH) +
+                                  (cc % RL) * 16) = rr[kb][i];
       }
   };
-
-  fetch(0);
-  stage(0);
-  __builtin_amdgcn_s_waitcnt(0);  // q rows and the first blocks are in: nothing pending
-  __syncthreads();
-  for (int jb0 = 0; jb0 < nblk; jb0 += KB) {
-    const int s = (jb0 / KB) & 1;
-    // The next stage's loads are in flight while this one is folded in.
-    fetch(jb0 + KB < nblk ? jb0 + KB : jb0);
-    __builtin_amdgcn_sched_barrier(0);
-    // 32 keys at a time; keys past the last block (stage rows loaded from
-    // the last block again) sit past every row's position and are masked.
+  // Fold LDS stage s (blocks jb0 ..) into the rows: 32 keys at a time; keys
+  // past the last block (stage rows loaded from the last block again) sit
+  // past every row's position and are masked.
+  auto fold = [&](int s, int jb0) {
 #pragma unroll
     for (int kc = 0; kc < prefill_stage_keys<D>() / KC; ++kc) {
       const int p0 = jb0 * BS + kc * KC;
       if (p0 < nblk * BS && p0 < wave_kend)
-        st.consume(s_kv[s] + kc * KC * PITCH, s_kv[s] + SK + kc * KC * PITCH, p0, rowpos,
-                   a.scale_log2, lane);
+        st.consume(s_kv[s] + kc * KC * KPITCH, s_kv[s] + SK + kc * KC * VPITCH, p0, rowpos,
+                   p0 + KC - 1 > wave_pos0, qsc.c, lane);
     }
-    stage(s ^ 1);
-    __syncthreads();
+  };
+  auto clampb = [&](int jb) { return jb < nblk ? jb : nblk - 1; };
+
+  fetch(r[0], 0);
+  stage(r[0], 0);
+  __builtin_amdgcn_s_waitcnt(0);  // q rows and the first blocks are in: nothing pending
+  __syncthreads();
+  if constexpr (kPrefillDepth == 1) {
+    for (int jb0 = 0; jb0 < nblk; jb0 += KB) {
+      const int s = (jb0 / KB) & 1;
+      // The next stage's loads are in flight while this one is folded in.
+      fetch(r[0], clampb(jb0 + KB));
+      __builtin_amdgcn_sched_barrier(0);
+      fold(s, jb0);
+      stage(r[0], s ^ 1);
+      __syncthreads();
+    }
+  } else {
+    // Two stages of loads in flight: while LDS stage s is folded in, the
+    // registers hold the next stage (staged to LDS after the fold) and the
+    // one after it is being loaded.  Unrolled by two so that each register
+    // set has fixed names.
+    fetch(r[1], clampb(KB));
+    for (int jb0 = 0; jb0 < nblk; jb0 += 2 * KB) {
+      fetch(r[0], clampb(jb0 + 2 * KB));
+      __builtin_amdgcn_sched_barrier(0);
+      fold(0, jb0);
+      stage(r[1], 1);
+      __syncthreads();
+      if (jb0 + KB >= nblk) break;
+      fetch(r[1], clampb(jb0 + 3 * KB));
+      __builtin_amdgcn_sched_barrier(0);
+      fold(1, jb0 + KB);
+      stage(r[0], 0);
+      __syncthreads();
+    }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no load left in flight past the loop
 
   if (bad) {
     for (int e = lane; e < NR * D; e += 64) {
@@ -311,7 +490,19 @@ extern "C" pa_status pa_paged_attention_prefill(
   a.num_kv_heads = num_kv_heads;
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
   a.row_groups = (int32_t)row_groups;
+  {
+    // Cost buckets of the longest-first order: T = tokens per row group keys
+    // each, widened so that the longest possible context fits the table.
+    const int64_t T = std::max<int64_t>(1, rows_per_wg / G);
+    const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
+    const int64_t nb = (max_tokens + T - 1) / T;
+    const int64_t widen = (nb + kMaxCostBuckets - 1) / kMaxCostBuckets;
+    a.bucket_width = (int32_t)(T * std::max<int64_t>(1, widen));
+    a.num_buckets = (int32_t)std::min<int64_t>(
+        kMaxCostBuckets, (max_tokens + a.bucket_width - 1) / a.bucket_width + 1);
+  }
   a.scale_log2 = scale * 1.4426950408889634f;
   const hipError_t err = launch_prefill(head_dim, block_size, G, a, num_seqs,
                                         static_cast<hipStream_t>(stream));
