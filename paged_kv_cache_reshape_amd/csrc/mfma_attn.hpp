@@ -159,20 +159,21 @@ struct RowTileAttn {
       for (int r = 0; r < 4; ++r) o[ht][dt][r] *= f[r];
   }
 
-  // One block, staged in LDS at kt (K rows, KPITCH bytes apart) and vt (V
-  // rows, VPITCH apart), token-major, every row finite.  pos0: sequence
-  // position of the block's first token; rowpos[ht]: this lane's row
-  // position (lane (j, n) -> row 16 ht + n).  With `masked` (uniform), keys
-  // past a row's position are masked (a row position of -1 masks all);
-  // without it every key is taken, so the caller clears it only for blocks
-  // that lie wholly at or before every live row's position.  c: QScale::c.
-  // All scores of the block are formed first, so that one kept maximum per
-  // row serves every weight of the block.
-  __device__ __forceinline__ void consume(const char* kt, const char* vt, int pos0,
-                                          const int (&rowpos)[HT], bool masked, float c,
-                                          int lane) {
+  // A block's fold is split in phases so that a caller can overlap the
+  // matrix-core products of one block with the vector work of another:
+  //   qk        raw scores q.k (matrix cores)
+  //   mask      causal mask (vector)
+  //   rowmax    block maximum per row and the lazy rescale (vector, branch)
+  //   weights   exp2, row sums and the hi/lo weight split (vector)
+  //   pv        O += P V (matrix cores)
+  // consume() runs them in order.
+  static constexpr int NP = TPB >= 2 ? TPB / 2 : 1;  // 16-token tile pairs
+  using Scores = f32x4[HT][TPB];    // lane (j, n): row n, tokens 4j .. 4j+3 of each tile
+  using Weights = bf16x8[HT][NP];   // p.v's A operand, one bf16x8 per tile pair
+
+  // K rows staged in LDS at kt (KPITCH bytes apart, token-major).
+  __device__ __forceinline__ void qk(const char* kt, Scores& x, int lane) const {
     const int n = lane & 15, j = lane >> 4;
-    f32x4 x[HT][TPB];  // raw scores q.k (-inf where masked)
 #pragma unroll
     for (int tt = 0; tt < TPB; ++tt) {
       bf16x8 ka[DK];
@@ -189,30 +190,42 @@ struct RowTileAttn {
         x[ht][tt] = s;
       }
     }
-    if (masked) {
+  }
+
+  // Keys past a row's position become -inf (a row position of -1 masks all).
+  __device__ __forceinline__ static void mask(Scores& x, int pos0, const int (&rowpos)[HT],
+                                              int lane) {
+    const int j = lane >> 4;
 #pragma unroll
-      for (int tt = 0; tt < TPB; ++tt) {
-        const int kp = pos0 + tt * 16 + 4 * j;  // key position of register 0
+    for (int tt = 0; tt < TPB; ++tt) {
+      const int kp = pos0 + tt * 16 + 4 * j;  // key position of register 0
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
+      for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            x[ht][tt][r] = kp + r <= rowpos[ht] ? x[ht][tt][r] : -INFINITY;
-      }
+        for (int r = 0; r < 4; ++r)
+          x[ht][tt][r] = kp + r <= rowpos[ht] ? x[ht][tt][r] : -INFINITY;
     }
-    // Weights as p.v's A operand, one bf16x8 per pair of 16-token tiles
-    // (lane (j, n): row n, tokens 4j .. 4j+3 of each tile of the pair).
-    constexpr int NP = TPB >= 2 ? TPB / 2 : 1;
-    bf16x8 ph[HT][NP], pl[HT][NP];
+  }
+
+  // Block maximum of each row (scaled by c > 0); rescales the state when a
+  // row's maximum passes the kept one by more than the lazy margin.
+  __device__ __forceinline__ void rowmax(const Scores& x, float c, int lane) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       float bmax = max4(x[ht][0]);
 #pragma unroll
       for (int tt = 1; tt < TPB; ++tt) bmax = fmaxf(bmax, max4(x[ht][tt]));
       bmax = fmaxf(bmax, lane_xor<16>(bmax));
-      bmax = fmaxf(bmax, lane_xor<32>(bmax)) * c;  // c > 0: the scaled maximum
+      bmax = fmaxf(bmax, lane_xor<32>(bmax)) * c;
       if (__builtin_amdgcn_ballot_w64(bmax > mth[ht]) != 0)
         rescale(ht, fmaxf(m[ht], bmax), lane);
+    }
+  }
+
+  // p = exp2(c x - m) against the kept maximum; row sums; hi/lo split.
+  __device__ __forceinline__ void weights(const Scores& x, float c, Weights& ph, Weights& pl) {
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
       float sum = 0.0f;
       uint32_t hw[TPB * 2], lw[TPB * 2];
 #pragma unroll
@@ -242,8 +255,13 @@ struct RowTileAttn {
         pl[ht][0] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], 0u, 0u));
       }
     }
-    // O += P V, one 16-wide d tile at a time; V arrives transposed from LDS.
-    const int L = lane & 15;
+  }
+
+  // O += P V, one 16-wide d tile at a time; V rows staged in LDS at vt
+  // (VPITCH bytes apart) arrive transposed.
+  __device__ __forceinline__ void pv(const char* vt, const Weights& ph, const Weights& pl,
+                                     int lane) {
+    const int j = lane >> 4, L = lane & 15;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       bf16x4 vb[TPB];
@@ -278,6 +296,27 @@ struct RowTileAttn {
         }
       }
     }
+  }
+
+  // One block, staged in LDS at kt (K rows, KPITCH bytes apart) and vt (V
+  // rows, VPITCH apart), token-major, every row finite.  pos0: sequence
+  // position of the block's first token; rowpos[ht]: this lane's row
+  // position (lane (j, n) -> row 16 ht + n).  With `masked` (uniform), keys
+  // past a row's position are masked (a row position of -1 masks all);
+  // without it every key is taken, so the caller clears it only for blocks
+  // that lie wholly at or before every live row's position.  c: QScale::c.
+  // All scores of the block are formed first, so that one kept maximum per
+  // row serves every weight of the block.
+  __device__ __forceinline__ void consume(const char* kt, const char* vt, int pos0,
+                                          const int (&rowpos)[HT], bool masked, float c,
+                                          int lane) {
+    Scores x;
+    qk(kt, x, lane);
+    if (masked) mask(x, pos0, rowpos, lane);
+    rowmax(x, c, lane);
+    Weights ph, pl;
+    weights(x, c, ph, pl);
+    pv(vt, ph, pl, lane);
   }
 
   // Row sums over all of the wave's tokens: lane (j, n) gets row 16 ht + n's.

@@ -25,7 +25,7 @@
 //     whose rows all end before the block skips it.
 // There is no split over key ranges, so no workspace and no merge: each
 // wave's state ends complete and is normalised and stored directly.
-#include "mfma_attn.hpp"
+#include "mfma_tile32.hpp"
 
 #include "decode_launch.hpp"
 
@@ -197,9 +197,10 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(
   // maximum update and one branch per call.
   constexpr int KC = PA_PREFILL_FOLD_KEYS < prefill_stage_keys<D>() ? PA_PREFILL_FOLD_KEYS
                                                                      : prefill_stage_keys<D>();
-  using Sh = TileShape<D, KC, NR>;
-  using T = RowTileAttn<D, KC, NR>;
-  constexpr int RL = Sh::RL, KPITCH = Sh::KPITCH, VPITCH = Sh::VPITCH, HT = Sh::HT;
+  using T = RowTile32Attn<D>;
+  static_assert(NR == 32 && KC % T::KC == 0, "a wave holds one 32-row tile");
+  constexpr int RL = D * 2 / 16;  // lanes per token row in a 16-byte global load
+  constexpr int KPITCH = T::Sh::KPITCH, VPITCH = T::Sh::VPITCH;
   constexpr int NT = NW * 64;
   constexpr int kChunks = BS * RL;  // 16-byte chunks of one block's rows, K or V
   static_assert(kChunks % 64 == 0, "a wave's chunks are all K or all V");
@@ -253,12 +254,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(
                          : nullptr;
       },
       qsc, lane);
-  int rowpos[HT];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const int R = wr0 + 16 * ht + (lane & 15);
-    rowpos[ht] = R < nrows ? first + R / G : -1;
-  }
+  const int rowpos = wr0 + (lane & 31) < nrows ? first + (wr0 + (lane & 31)) / G : -1;
   // Keys this wave's rows reach (0 if it has no rows); chunks ending at or
   // before its first row's position need no causal mask.
   const int wave_kend = wr0 < nrows ? first + (min(nrows, wr0 + NR) - 1) / G + 1 : 0;
@@ -338,9 +334,15 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(
 #pragma unroll
     for (int kc = 0; kc < prefill_stage_keys<D>() / KC; ++kc) {
       const int p0 = jb0 * BS + kc * KC;
-      if (p0 < nblk * BS && p0 < wave_kend)
-        st.consume(s_kv[s] + kc * KC * KPITCH, s_kv[s] + SK + kc * KC * VPITCH, p0, rowpos,
-                   p0 + KC - 1 > wave_pos0, qsc.c, lane);
+      if (p0 < nblk * BS && p0 < wave_kend) {
+#pragma unroll
+        for (int t = 0; t < KC / T::KC; ++t) {
+          const int pt = p0 + t * T::KC;
+          st.consume(s_kv[s] + (kc * KC + t * T::KC) * KPITCH,
+                     s_kv[s] + SK + (kc * KC + t * T::KC) * VPITCH, pt, rowpos,
+                     pt + T::KC - 1 > wave_pos0, qsc.c, lane);
+        }
+      }
     }
   };
   auto clampb = [&](int jb) { return jb < nblk ? jb : nblk - 1; };
