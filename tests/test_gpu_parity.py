@@ -607,6 +607,34 @@ def test_prefill_ragged_with_empty_and_bad_sequences():
     assert np.isnan(got[int(start[bad]):int(start[bad + 1])]).all()
 
 
+def test_prefill_many_sequences():
+    """700 sequences (more than a workgroup has threads, so each thread ranks
+    several), short prompts and chunks, every seventh sequence with no new
+    token: every row of the longest-first schedule is computed once."""
+    w = synth.Workload("pf_many", 700, 4, 2, 64, 16, "bf16", ("uniform", 1, 120), seed=57,
+                       query=("uniform", 1, 120))
+    base = synth.make_prefill_inputs(w)
+    qlen = base["query_lens"].copy()
+    qlen[::7] = 0
+    inp = synth.make_prefill_inputs(w, query_lens=qlen)
+    say("prefill 700 sequences, tokens", int(inp["query_start"][-1]))
+    _, out = prefill_gpu(inp)
+    ref, _ = prefill_oracle(inp)
+    G.assert_close(G.host_f64(out), ref, "bf16", "700 sequences")
+
+
+def test_prefill_wide_cost_buckets():
+    """Block tables long enough (262,144 tokens) that the ranking's cost
+    buckets are widened to fit its table; the prompts themselves are short."""
+    w = synth.Workload("pf_wide", 5, 8, 2, 128, 16, "bf16", ("uniform", 50, 700), seed=58,
+                       query=("uniform", 1, 700), max_blocks=16384)
+    inp = synth.make_prefill_inputs(w)
+    say("prefill wide buckets, tokens", int(inp["query_start"][-1]))
+    _, out = prefill_gpu(inp)
+    ref, _ = prefill_oracle(inp)
+    G.assert_close(G.host_f64(out), ref, "bf16", "wide buckets")
+
+
 @pytest.mark.parametrize("name", ["pf_g2_d128_bs16", "pf_full_g32_d128_bs32",
                                   "pf_g4_d64_bs16"])
 def test_prefill_first_token_exact(name):
