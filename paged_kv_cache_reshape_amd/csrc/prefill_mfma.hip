@@ -189,14 +189,24 @@ constexpr int kPrefillRows = 32;  // query rows per wave
 template <int D>
 constexpr int prefill_stage_keys() { return D == 64 ? 32 : PA_PREFILL_STAGE_KEYS; }
 
-template <int D, int BS, int G, int NW>
+// KS = 1: each wave folds every key of the workgroup's range into its 32
+// rows.  KS = 2: the waves form NW / 2 row sets x 2 key halves -- wave w and
+// wave w + NW/2 hold the same rows and fold alternate 32-key folds (the two
+// of a 64-key stage, or alternate 32-key stages) -- and combine their states
+// through LDS at the end.  That halves a
+// workgroup's serial key loop (and doubles the workgroups) for batches with
+// few new rows against long contexts (chunks after a cached prefix).
+template <int D, int BS, int G, int NW, int KS>
 __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(PrefillArgs a) {
+  static_assert(KS == 1 || KS == 2, "one or two key halves");
   constexpr int NR = kPrefillRows;
+  constexpr int RW = NW / KS;  // row sets (waves with distinct rows)
   // Keys folded per call: a whole stage (two or four 16-token tiles, so p.v
   // runs on v_mfma_f32_16x16x32_bf16 whatever the block size); one running
   // maximum update and one branch per call.
-  constexpr int KC = PA_PREFILL_FOLD_KEYS < prefill_stage_keys<D>() ? PA_PREFILL_FOLD_KEYS
-                                                                     : prefill_stage_keys<D>();
+  constexpr int SKEYS = prefill_stage_keys<D>();
+  constexpr int KC = KS == 2 ? 32
+                     : PA_PREFILL_FOLD_KEYS < SKEYS ? PA_PREFILL_FOLD_KEYS : SKEYS;
   using T = RowTile32Attn<D>;
   static_assert(NR == 32 && KC % T::KC == 0, "a wave holds one 32-row tile");
   constexpr int RL = D * 2 / 16;  // lanes per token row in a 16-byte global load
@@ -205,16 +215,23 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(
   constexpr int kChunks = BS * RL;  // 16-byte chunks of one block's rows, K or V
   static_assert(kChunks % 64 == 0, "a wave's chunks are all K or all V");
   constexpr int NCH = (2 * kChunks + NT - 1) / NT;  // chunks per thread per block, K and V
-  constexpr int KB = prefill_stage_keys<D>() / BS;              // blocks per stage
-  constexpr int SK = prefill_stage_keys<D>() * KPITCH;          // one stage's K rows
-  constexpr int SV = prefill_stage_keys<D>() * VPITCH;          // one stage's V rows
+  constexpr int KB = SKEYS / BS;              // blocks per stage
+  constexpr int SK = SKEYS * KPITCH;          // one stage's K rows
+  constexpr int SV = SKEYS * VPITCH;          // one stage's V rows
   // [stage][K rows | V rows]: the stage's KB blocks are consecutive logical
   // blocks, so row t of a stage is key position (first block) * BS + t.
-  __shared__ __attribute__((aligned(16))) char s_kv[2][SK + SV];
+  // With key halves the same bytes afterwards hold the halves' exchange.
+  constexpr int NV = 2 + T::DT * 16;  // floats per lane of a wave's state
+  constexpr int kStages = 2 * (SK + SV);
+  constexpr int kExchange = KS == 2 ? RW * NV * 64 * 4 : 0;
+  __shared__ __attribute__((aligned(16))) char s_raw[kStages > kExchange ? kStages : kExchange];
+  char (*s_kv)[SK + SV] = reinterpret_cast<char (*)[SK + SV]>(s_raw);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rw = wave % RW;  // row set
+  const int kh = wave / RW;  // key half (always 0 with KS = 1)
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
   // Workgroup L takes kv head L % Hkv (so, with Hkv a multiple of the eight
   // XCDs that workgroups are dealt to in turn, a head's K/V stays in one
@@ -222,14 +239,14 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(
   const int L = blockIdx.y * gridDim.x + blockIdx.x;
   const int g = L % Hkv;
   int b, rg;
-  if (!pick_unit<G, NW * NR, NT>(a, a.max_blocks * BS, L / Hkv, b, rg)) return;
+  if (!pick_unit<G, RW * NR, NT>(a, a.max_blocks * BS, L / Hkv, b, rg)) return;
   const int qs = a.query_start[b];
   const int nq = a.query_start[b + 1] - qs;
   const int ctx = a.context_lens[b];
   const int nrows = nq * G;
-  const int r0 = rg * NW * NR;
+  const int r0 = rg * RW * NR;
   if (r0 >= nrows) return;
-  const int r_end = min(nrows, r0 + NW * NR);
+  const int r_end = min(nrows, r0 + RW * NR);
   uint16_t* out = static_cast<uint16_t*>(a.out);
   auto out_at = [&](int r, int d) -> size_t {
     return ((size_t)(qs + r / G) * Hq + (size_t)g * G + r % G) * D + d;
@@ -242,7 +259,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(
   const int first = ctx - nq;  // position of new token 0
   const int nblk = (first + (r_end - 1) / G + 1 + BS - 1) / BS;
 
-  const int wr0 = r0 + wave * NR;  // this wave's first row
+  const int wr0 = r0 + rw * NR;  // this wave's first row
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   T st;
   const QScale qsc(a.scale_log2);
@@ -332,9 +349,9 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(
   // past every row's position and are masked.
   auto fold = [&](int s, int jb0) {
 #pragma unroll
-    for (int kc = 0; kc < prefill_stage_keys<D>() / KC; ++kc) {
+    for (int kc = 0; kc < SKEYS / KC; ++kc) {
       const int p0 = jb0 * BS + kc * KC;
-      if (p0 < nblk * BS && p0 < wave_kend) {
+      if ((p0 / T::KC) % KS == kh && p0 < nblk * BS && p0 < wave_kend) {
 #pragma unroll
         for (int t = 0; t < KC / T::KC; ++t) {
           const int pt = p0 + t * T::KC;
@@ -384,11 +401,41 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(
   __builtin_amdgcn_s_waitcnt(0);  // no load left in flight past the loop
 
   if (bad) {
-    for (int e = lane; e < NR * D; e += 64) {
-      const int R = wr0 + e / D;
-      if (R < nrows) out[out_at(R, e % D)] = 0x7FC0;
-    }
+    if (kh == 0)
+      for (int e = lane; e < NR * D; e += 64) {
+        const int R = wr0 + e / D;
+        if (R < nrows) out[out_at(R, e % D)] = 0x7FC0;
+      }
     return;
+  }
+  if constexpr (KS == 2) {
+    // The key-half-1 wave of each row set hands its state (max, sum, output
+    // registers) to the key-half-0 wave through LDS, lane for lane: both hold
+    // the same rows in the same register layout.
+    float* s_x = reinterpret_cast<float*>(s_raw) + rw * NV * 64;
+    __syncthreads();  // every wave is done with the stages
+    if (kh == 1) {
+      s_x[lane] = st.m;
+      s_x[64 + lane] = st.l;
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s_x[(2 + dt * 16 + r) * 64 + lane] = st.o[dt][r];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m1 = s_x[lane], l1 = s_x[64 + lane];
+    const float M = fmaxf(st.m, m1);
+    const float a0 = fast_exp2(st.m - M), a1 = fast_exp2(m1 - M);  // this lane's row
+    st.l = st.l * a0 + l1 * a1;
+    st.m = M;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float f0 = T::from_row(a0, lane, r), f1 = T::from_row(a1, lane, r);
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt)
+        st.o[dt][r] = st.o[dt][r] * f0 + s_x[(2 + dt * 16 + r) * 64 + lane] * f1;
+    }
   }
   st.store_rows(
       [&](int row, int d, float v) {
@@ -401,23 +448,26 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(
 namespace {
 
 template <int D, int BS, int G>
-hipError_t launch_prefill_t(const PrefillArgs& a, int num_seqs, hipStream_t stream) {
+hipError_t launch_prefill_t(const PrefillArgs& a, int num_seqs, int ks, hipStream_t stream) {
   dim3 grid(num_seqs * a.num_kv_heads, a.row_groups);
-  prefill_mfma_kernel<D, BS, G, kPrefillWaves><<<grid, kPrefillWaves * 64, 0, stream>>>(a);
+  if (ks == 2)
+    prefill_mfma_kernel<D, BS, G, kPrefillWaves, 2><<<grid, kPrefillWaves * 64, 0, stream>>>(a);
+  else
+    prefill_mfma_kernel<D, BS, G, kPrefillWaves, 1><<<grid, kPrefillWaves * 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(int D, int BS, int G, const PrefillArgs& a, int num_seqs,
+hipError_t launch_prefill(int D, int BS, int G, const PrefillArgs& a, int num_seqs, int ks,
                           hipStream_t s) {
   auto by_g = [&](auto d, auto bs) -> hipError_t {
     constexpr int Dv = decltype(d)::value, BSv = decltype(bs)::value;
     switch (G) {
-      case 1: return launch_prefill_t<Dv, BSv, 1>(a, num_seqs, s);
-      case 2: return launch_prefill_t<Dv, BSv, 2>(a, num_seqs, s);
-      case 4: return launch_prefill_t<Dv, BSv, 4>(a, num_seqs, s);
-      case 8: return launch_prefill_t<Dv, BSv, 8>(a, num_seqs, s);
-      case 16: return launch_prefill_t<Dv, BSv, 16>(a, num_seqs, s);
-      case 32: return launch_prefill_t<Dv, BSv, 32>(a, num_seqs, s);
+      case 1: return launch_prefill_t<Dv, BSv, 1>(a, num_seqs, ks, s);
+      case 2: return launch_prefill_t<Dv, BSv, 2>(a, num_seqs, ks, s);
+      case 4: return launch_prefill_t<Dv, BSv, 4>(a, num_seqs, ks, s);
+      case 8: return launch_prefill_t<Dv, BSv, 8>(a, num_seqs, ks, s);
+      case 16: return launch_prefill_t<Dv, BSv, 16>(a, num_seqs, ks, s);
+      case 32: return launch_prefill_t<Dv, BSv, 32>(a, num_seqs, ks, s);
     }
     return hipErrorInvalidValue;
   };
@@ -465,7 +515,15 @@ extern "C" pa_status pa_paged_attention_prefill(
               block_size);
     return PA_ERR_UNSUPPORTED;
   }
-  const int64_t rows_per_wg = (int64_t)kPrefillWaves * kPrefillRows;
+  // Key halves per workgroup (see prefill_mfma_kernel): two when the block
+  // table spans at least four times the longest query, i.e. few new rows
+  // against long contexts.  PAGEDATTN_PREFILL_KSPLIT=1|2 forces either.
+  int ks = (int64_t)max_blocks_per_seq * block_size >= 4 * (int64_t)max_query_len ? 2 : 1;
+  if (const char* env = getenv("PAGEDATTN_PREFILL_KSPLIT")) {
+    if (env[0] == '1') ks = 1;
+    if (env[0] == '2') ks = 2;
+  }
+  const int64_t rows_per_wg = (int64_t)kPrefillWaves * kPrefillRows / ks;
   const int64_t row_groups = ((int64_t)max_query_len * G + rows_per_wg - 1) / rows_per_wg;
   if (row_groups > 65535 || (int64_t)num_seqs * num_kv_heads > 0x7FFFFFFF) {
     set_error("max_query_len=%d too large for one launch", max_query_len);
@@ -506,7 +564,7 @@ extern "C" pa_status pa_paged_attention_prefill(
         kMaxCostBuckets, (max_tokens + a.bucket_width - 1) / a.bucket_width + 1);
   }
   a.scale_log2 = scale * 1.4426950408889634f;
-  const hipError_t err = launch_prefill(head_dim, block_size, G, a, num_seqs,
+  const hipError_t err = launch_prefill(head_dim, block_size, G, a, num_seqs, ks,
                                         static_cast<hipStream_t>(stream));
   if (err != hipSuccess) {
     set_error("prefill launch failed: %s", hipGetErrorString(err));

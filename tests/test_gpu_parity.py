@@ -572,20 +572,27 @@ def prefill_oracle(inp):
                           inp["query_start"], inp["scale"], inp["workload"].dtype), (k, v)
 
 
+@pytest.mark.parametrize("ks", ["1", "2"])
 @pytest.mark.parametrize("name", list(PF))
-def test_prefill_matches_oracle(name):
+def test_prefill_matches_oracle(name, ks, monkeypatch):
+    """Every prefill shape, with each wave folding all of its keys (1) and
+    with the keys split between two waves per row set (2)."""
+    monkeypatch.setenv("PAGEDATTN_PREFILL_KSPLIT", ks)
     w = PF[name]
     inp = synth.make_prefill_inputs(w)
-    say("prefill", name, "rows", int(inp["query_start"][-1]) * (w.num_q_heads // w.num_kv_heads))
+    say("prefill", name, "key halves", ks, "rows",
+        int(inp["query_start"][-1]) * (w.num_q_heads // w.num_kv_heads))
     d, out = prefill_gpu(inp)
     ref, (k_ref, _) = prefill_oracle(inp)
     assert np.array_equal(G.host_storage(d["k_cache"]), k_ref)
     G.assert_close(G.host_f64(out), ref, "bf16", name)
 
 
-def test_prefill_ragged_with_empty_and_bad_sequences():
+@pytest.mark.parametrize("ks", ["1", "2"])
+def test_prefill_ragged_with_empty_and_bad_sequences(ks, monkeypatch):
     """A sequence with no new tokens writes nothing; a sequence claiming more
     new tokens than positions gets NaN rows; the others are unaffected."""
+    monkeypatch.setenv("PAGEDATTN_PREFILL_KSPLIT", ks)
     w = PF["pf_g2_d128_bs16"]
     inp = synth.make_prefill_inputs(w, query_lens=np.array([37, 0, 250, 5], dtype=np.int32))
     ctx = inp["context_lens"].copy()
