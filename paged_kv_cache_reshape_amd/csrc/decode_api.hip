@@ -60,8 +60,8 @@ bool use_mfma(int dtype, int D, int bs, int G) {
   return !(env && strcmp(env, "valu") == 0);
 }
 
-// Experimental: PAGEDATTN_MERGE=separate / inkernel forces where split
-// sequences are merged.
+// PAGEDATTN_MERGE=separate / inkernel forces where split sequences are
+// merged (the tests run both paths).
 bool deferred_merge(int max_parts) {
   const char* env = getenv("PAGEDATTN_MERGE");
   if (env && strcmp(env, "separate") == 0) return true;

@@ -178,11 +178,7 @@ __device__ __forceinline__ bool pick_unit(const PrefillArgs& a, int max_tokens, 
 #ifndef PA_PREFILL_FOLD_KEYS
 #define PA_PREFILL_FOLD_KEYS 64
 #endif
-#ifndef PA_PREFILL_DEPTH
-#define PA_PREFILL_DEPTH 2
-#endif
 constexpr int kPrefillWaves = PA_PREFILL_WAVES;
-constexpr int kPrefillDepth = PA_PREFILL_DEPTH;  // stages of K/V loads in flight (1 or 2)
 constexpr int kPrefillRows = 32;  // query rows per wave
 // Keys per LDS stage (several blocks): 64, or 32 at head_dim 64, where the
 // workgroup is held to 128 VGPRs so that two fit on a compute unit.
@@ -295,7 +291,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(
       (const __attribute__((address_space(4))) int32_t*)(a.block_tables +
                                                           (size_t)b * a.max_blocks);
   bool bad = false;  // a block id outside the pool: rows become NaN
-  uint4 r[kPrefillDepth][KB][NCH];  // stages of K/V rows in flight
+  uint4 r[2][KB][NCH];  // two stages of K/V rows in flight
   auto chunk = [&](int i) { return (tid + i * NT) % (2 * kChunks); };
   // Loads of blocks jb0 .. jb0 + KB - 1 into register set rs (ids past the
   // last block read the last one again: in range, never folded in).
@@ -368,17 +364,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void prefill_mfma_kernel(
   stage(r[0], 0);
   __builtin_amdgcn_s_waitcnt(0);  // q rows and the first blocks are in: nothing pending
   __syncthreads();
-  if constexpr (kPrefillDepth == 1) {
-    for (int jb0 = 0; jb0 < nblk; jb0 += KB) {
-      const int s = (jb0 / KB) & 1;
-      // The next stage's loads are in flight while this one is folded in.
-      fetch(r[0], clampb(jb0 + KB));
-      __builtin_amdgcn_sched_barrier(0);
-      fold(s, jb0);
-      stage(r[0], s ^ 1);
-      __syncthreads();
-    }
-  } else {
+  {
     // Two stages of loads in flight: while LDS stage s is folded in, the
     // registers hold the next stage (staged to LDS after the fold) and the
     // one after it is being loaded.  Unrolled by two so that each register
