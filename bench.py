@@ -47,7 +47,7 @@ HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_reshape_amd", "csrc", f)
                for f in ("decode_partition.hip", "decode_mfma.hip", "attn_common.hpp",
-                         "common.hpp", "decode_launch.hpp", "decode_api.hip")]
+                         "mfma_attn.hpp", "common.hpp", "decode_launch.hpp", "decode_api.hip")]
 
 
 def algorithmic_bytes(inp: dict) -> dict:
