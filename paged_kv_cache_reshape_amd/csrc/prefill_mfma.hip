@@ -511,8 +511,11 @@ extern "C" pa_status pa_paged_attention_prefill(
   }
   const int64_t rows_per_wg = (int64_t)kPrefillWaves * kPrefillRows / ks;
   const int64_t row_groups = ((int64_t)max_query_len * G + rows_per_wg - 1) / rows_per_wg;
-  if (row_groups > 65535 || (int64_t)num_seqs * num_kv_heads > 0x7FFFFFFF) {
-    set_error("max_query_len=%d too large for one launch", max_query_len);
+  // Workgroups are numbered blockIdx.y * gridDim.x + blockIdx.x in 32 bits.
+  if (row_groups > 65535 || (int64_t)num_seqs * num_kv_heads * row_groups > 0x7FFFFFFF) {
+    set_error("num_seqs=%d x num_kv_heads=%d x %lld row groups (max_query_len=%d) is too "
+              "large for one launch", num_seqs, num_kv_heads, (long long)row_groups,
+              max_query_len);
     return PA_ERR_INVALID_ARGUMENT;
   }
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;

@@ -126,6 +126,9 @@ def test_prefill_argument_checks(lib):
     assert call(qs=None) == INVALID
     assert call(q=24) == INVALID                # misaligned
     assert call(mq=1 << 30) == INVALID          # launch too large
+    # 2^20 sequences x 8 kv heads x 256 row groups: more workgroups than a
+    # 32-bit workgroup number holds
+    assert call(B=1 << 20, Hq=8, Hkv=8, mq=65536) == INVALID
     assert call(T=0, q=None, out=None) == OK    # nothing to do
     assert call(B=0, qs=None) == OK
 
