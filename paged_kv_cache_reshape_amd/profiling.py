@@ -8,6 +8,9 @@ Commands (run on the CSV files a GPU run wrote):
   python -m paged_kv_cache_reshape_amd.profiling traffic FETCH_CSV WRITE_CSV \\
       --workload qwen3_0p6b --partition-size 1024 --command "<...>"
 
+  python -m paged_kv_cache_reshape_amd.profiling counters OUT_MD --kernel NAME \\
+      --command "<...>" COUNTER_CSV [COUNTER_CSV ...]
+
 ``traffic`` scales the per-dispatch FETCH_SIZE and WRITE_SIZE of the decode
 kernel by what the same counters read for the plain copy kernels in the same
 run (PyTorch cloning one K cache, a copy of known size), and records the hash
@@ -120,6 +123,25 @@ def traffic_record(fetch_csv: str, write_csv: str, workload: str, partition_size
     return rec
 
 
+def counters_summary(csvs: list, kernel: str, out_md: str, command: str) -> dict:
+    """Average per dispatch of every counter collected for the kernels whose
+    name contains `kernel`, over one or more counter-collection CSVs (one
+    rocprofv3 --pmc pass each)."""
+    agg = collections.defaultdict(list)
+    for path in csvs:
+        for r in csv.DictReader(open(path)):
+            if kernel in r["Kernel_Name"]:
+                agg[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    avg = {k: sum(v) / len(v) for k, v in sorted(agg.items())}
+    lines = [f"# Hardware counters of `{kernel}`", "", "Commands (one pass each):", "", "```",
+             command, "```", "", "| counter | average per dispatch | dispatches |",
+             "|---|---|---|"]
+    for k, v in avg.items():
+        lines.append(f"| {k} | {v:.6g} | {len(agg[k])} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    return avg
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -133,9 +155,16 @@ def main(argv=None) -> int:
     f.add_argument("--workload", default="qwen3_0p6b")
     f.add_argument("--partition-size", type=int, required=True)
     f.add_argument("--command", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("out_md")
+    c.add_argument("csvs", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--command", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         trace_summary(a.stats_csv, a.out_md, a.command)
+    elif a.cmd == "counters":
+        print(json.dumps(counters_summary(a.csvs, a.kernel, a.out_md, a.command), indent=1))
     else:
         print(json.dumps(traffic_record(a.fetch_csv, a.write_csv, a.workload,
                                         a.partition_size, a.command), indent=1))
