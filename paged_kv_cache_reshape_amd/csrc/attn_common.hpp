@@ -145,12 +145,13 @@ struct RowAttn {
 
   // K and V rows of one block: kb / vb point at this lane's chunk of the
   // block's first row for this kv head; rows are tok_stride elements apart.
+  // Streaming (non-temporal) loads: each row is read once.
   __device__ __forceinline__ static void fetch(const S* kb, const S* vb, size_t tok_stride,
                                                uint4 (&kr)[NI], uint4 (&vr)[NI]) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) kr[i] = load_chunk(kb + (size_t)i * ROWS * tok_stride);
+    for (int i = 0; i < NI; ++i) kr[i] = load_stream(kb + (size_t)i * ROWS * tok_stride);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) vr[i] = load_chunk(vb + (size_t)i * ROWS * tok_stride);
+    for (int i = 0; i < NI; ++i) vr[i] = load_stream(vb + (size_t)i * ROWS * tok_stride);
   }
 
   // Fold one block into the state.  pos0: sequence position of this lane's

@@ -26,6 +26,15 @@ struct BF16 {
 __device__ __forceinline__ uint4 load_chunk(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
+// The same load for data read once per launch (the decode's K/V stream):
+// marked non-temporal ("nt"), so the caches treat the lines as streaming.
+// Measured on MI355X: 1-7% less time on the decode batches than plain loads
+// with the same addresses; scope bits alone (sc1) changed nothing.
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ void store_chunk(void* p, uint4 v) {
   *reinterpret_cast<uint4*>(p) = v;
 }

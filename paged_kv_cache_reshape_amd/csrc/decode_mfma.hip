@@ -13,8 +13,8 @@
 // the G heads of the sequence's newest token, all at its position.  Per
 // block, each wave loads K and V rows with full-row coalesced 16-byte loads
 // (the pattern that measured fastest; tokens past the context read the
-// block's first token, in range and finite, and are masked) and stages them
-// in its own LDS tile.
+// block's first token, in range and finite, and are masked), marked
+// non-temporal since each is read once, and stages them in its own LDS tile.
 #include "mfma_attn.hpp"
 
 #include "decode_launch.hpp"
@@ -88,10 +88,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      kr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off[i], 0, 0));
+      kr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off[i], 0, kLoadStreaming));
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      vr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off[i], 0, 0));
+      vr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off[i], 0, kLoadStreaming));
   };
   char* kt = s_raw + wave * (KTILE + VTILE);
   char* vt = kt + KTILE;

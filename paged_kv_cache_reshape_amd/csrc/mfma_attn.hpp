@@ -54,6 +54,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Buffer resource word 3 for gfx9-family raw buffer loads (32-bit data
 // format; accesses are range-checked against num_records bytes).
 constexpr int kBufferRsrcWord3 = 0x00020000;
+// Cache-policy operand of a buffer load that reads data once per launch:
+// the non-temporal bit ("nt", bit 1 on gfx950).
+constexpr int kLoadStreaming = 2;
 
 template <int D, int BS, int NR>
 struct TileShape {
