@@ -474,21 +474,67 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
   const int wg_elems = hpw * G * D;
   const size_t out_base = ((size_t)b * a.num_q_heads + (size_t)gg * hpw * G) * D;
 
+  // Row r = hwe * G + hh of the group (the order of the output rows) is held
+  // by waves w0(r) + hpw * HS * t, t < nwt, head h(r).  With large query
+  // groups (many elements per thread, shares from eight waves) its maximum,
+  // sum and the factor of each wave's share are worked out once per row and
+  // used by the row's D elements; with small ones each element works them
+  // out itself, since there the extra barrier costs more than the
+  // exponentials it saves (measured on MI355X: MQA batch 25.2 -> 24.3 us,
+  // Qwen3 batch 33.8 -> 34.1 us when shared).  Same operations in the same
+  // order either way, so the results are the same bits.  The shared factors
+  // live in the merge's LDS area, not used before the combine is over:
+  // nwt * rows = NW * GW factors fit in s_pm, 2 * rows in s_pl.
+  constexpr bool kRowFactors = G >= 8;
+  static_assert(NW * GW <= 64 * G, "combine factors must fit the merge's LDS area");
+  __shared__ float s_pm[64][G];
+  __shared__ float s_pl[64][G];
+  const int rows = hpw * G;
+  float* s_fac = &s_pm[0][0];  // [t][r]: t * rows + r
+  float* s_rm = &s_pl[0][0];
+  float* s_rl = s_rm + rows;
+  if constexpr (kRowFactors) {
+    for (int r = tid; r < rows; r += NT) {
+      const int hwe = r / G, hh = r % G;
+      const int w0 = hwe + hpw * (hh / GW);
+      const int h = hh % GW;
+      float M = kNoMax;
+      for (int t = 0; t < nwt; ++t) M = fmaxf(M, s_m[w0 + hpw * HS * t][h]);
+      float L = 0.0f;
+      for (int t = 0; t < nwt; ++t) {
+        const int w = w0 + hpw * HS * t;
+        const float f = fast_exp2(s_m[w][h] - M);
+        s_fac[t * rows + r] = f;
+        L += s_l[w][h] * f;
+      }
+      s_rm[r] = M;
+      s_rl[r] = poisoned ? __builtin_nanf("") : L;
+    }
+    __syncthreads();
+  }
   for (int e = tid; e < wg_elems; e += NT) {
     const int hwe = e / (G * D), rem = e % (G * D);
     const int hh = rem / D, d = rem % D;
+    const int r = e / D;
     const int w0 = hwe + hpw * (hh / GW);
     const int h = hh % GW;
-    float M = kNoMax;
-    for (int t = 0; t < nwt; ++t) M = fmaxf(M, s_m[w0 + hpw * HS * t][h]);
-    float L = 0.0f, A = 0.0f;
-    for (int t = 0; t < nwt; ++t) {
-      const int w = w0 + hpw * HS * t;
-      const float f = fast_exp2(s_m[w][h] - M);
-      L += s_l[w][h] * f;
-      A += s_acc[w][h][d] * f;
+    float M, L, A = 0.0f;
+    if constexpr (kRowFactors) {
+      for (int t = 0; t < nwt; ++t) A += s_acc[w0 + hpw * HS * t][h][d] * s_fac[t * rows + r];
+      M = s_rm[r];
+      L = s_rl[r];
+    } else {
+      M = kNoMax;
+      for (int t = 0; t < nwt; ++t) M = fmaxf(M, s_m[w0 + hpw * HS * t][h]);
+      L = 0.0f;
+      for (int t = 0; t < nwt; ++t) {
+        const int w = w0 + hpw * HS * t;
+        const float f = fast_exp2(s_m[w][h] - M);
+        L += s_l[w][h] * f;
+        A += s_acc[w][h][d] * f;
+      }
+      if (poisoned) L = __builtin_nanf("");
     }
-    if (poisoned) L = __builtin_nanf("");
     if (nparts == 1) {
       store_out(DT{}, a.out, out_base + e, A / L);
     } else {
@@ -518,8 +564,6 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
   // Rows of partition p for query head qh of kv head x of the group: pieces
   // of one kv head are max_parts * G rows apart, so merge one kv head at a
   // time.
-  __shared__ float s_pm[64][G];
-  __shared__ float s_pl[64][G];
   const size_t head_rows = (size_t)a.max_parts * G;
   const size_t grp_base = ((size_t)b * Hkv + (size_t)gg * hpw) * head_rows;
   for (int x = 0; x < hpw; ++x) {
