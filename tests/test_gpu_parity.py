@@ -318,7 +318,8 @@ def test_nan_poison_bit_identical(name):
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("name,ps", [("qwen3_0p6b", 64), ("qwen3_0p6b", 256), ("long_splitk", 512)])
+@pytest.mark.parametrize("name,ps", [("qwen3_0p6b", 64), ("qwen3_0p6b", 256), ("long_splitk", 512),
+                                     ("bf16_d128_bs16_g16", 128), ("bf16_d128_bs16_g16", 32)])
 def test_rerun_bit_identical(name, ps):
     """P14: partitions finish in any order, the merge does not depend on it."""
     inp = inputs_for(name)
@@ -344,27 +345,31 @@ def test_empty_sequences_give_zero_rows():
 
 
 @pytest.mark.parametrize("merge", ["inkernel", "separate"])
-def test_bad_table_entries_give_nan_rows_only(merge, monkeypatch):
+@pytest.mark.parametrize("name,ps", [("qwen3_0p6b", 256), ("bf16_d128_bs16_g16", 128)])
+def test_bad_table_entries_give_nan_rows_only(name, ps, merge, monkeypatch):
     """A block id outside the pool, or a length past the table, is never
     dereferenced: that sequence's rows become NaN, the others are unchanged
-    (with split sequences merged in the partition kernel or after it)."""
+    (with split sequences merged in the partition kernel or after it; the
+    vector-ALU kernel and the matrix-core one)."""
     monkeypatch.setenv("PAGEDATTN_MERGE", merge)
-    inp = inputs_for("qwen3_0p6b")
-    say("decode bad table entries, merge", merge)
+    inp = inputs_for(name)
+    w = inp["workload"]
+    B, bs = w.num_seqs, w.block_size
+    say("decode bad table entries", name, "partition", ps, "merge", merge)
     d = G.upload(inp)
-    base = G.host_storage(gpu_step(d, 256))
+    base = G.host_storage(gpu_step(d, ps))
     t = inp["block_tables"].copy()
     ctx = inp["context_lens"].copy()
-    t[2, 0] = inp["num_blocks"]        # one past the pool
-    t[4, (ctx[4] - 1) // 16] = -5      # negative, in the last used block
-    ctx[6] = 129 * 16                  # longer than the table
+    bad = [1, B // 2, B - 1]
+    t[bad[0], 0] = inp["num_blocks"]                  # one past the pool
+    t[bad[1], (ctx[bad[1]] - 1) // bs] = -5           # negative, in the last used block
+    ctx[bad[2]] = (t.shape[1] + 1) * bs               # longer than the table
     d2 = dict(d, block_tables=torch.from_numpy(t).cuda(),
               context_lens=torch.from_numpy(ctx).cuda())
-    out = gpu_step(d2, 256, write=False)
+    out = gpu_step(d2, ps, write=False)
     got = G.host_f64(out)
-    bad = [2, 4, 6]
     assert np.all(np.isnan(got[bad]))
-    keep = [b for b in range(32) if b not in bad]
+    keep = [b for b in range(B) if b not in bad]
     assert np.array_equal(G.host_storage(out)[keep], base[keep])
 
 
