@@ -1,8 +1,10 @@
 """Benchmark of one decode step (paged KV write + paged decode attention) on one GPU.
 
-A step is one pass of the whole path over one synthetic batch: write each
-sequence's new K/V row with ``reshape_and_cache``, then ``paged_attention_decode``
-over the updated caches.  Default workload: the Qwen3-0.6B-shaped batch
+A step is one pass of the whole path over one synthetic batch: each
+sequence's new K/V row is written into the paged caches and the decode runs
+over the updated caches, both in one launch (``decode_step``, the write fused
+into the decode kernel; the same bits as ``reshape_and_cache`` followed by
+``paged_attention_decode``, whose two-launch step is timed too).  Default workload: the Qwen3-0.6B-shaped batch
 (B=32, Hq=16, Hkv=8, D=128, block_size=16, context lengths uniform in
 [128, 2048], bf16 storage, float32 accumulation).
 
@@ -12,14 +14,16 @@ through R identical copies of the KV pool (>= 1.25 GiB together).
 
 Prints one JSON line.  ``value`` is the step's algorithmic bytes (KV rows
 read, q read, output written, block-table entries, the write's rows) divided by
-the step time.  ``roofline`` is for the decode kernel alone: algorithmic bytes
-per launch over its mean launch time, from HIP events on the stream it runs on
-around K back-to-back launches.  ``graph_us_per_step`` is the same step
-replayed from a HIP graph.  ``decode_us_loops`` / ``decode_us_median`` are
-five more loops of decode launches timed one by one; ``mall_resident`` is the
+the step time.  ``roofline`` is for the step's kernel (the decode with the
+write fused in): its algorithmic bytes per launch over its mean launch time in
+the timed region, from HIP events on the stream it runs on around the K
+back-to-back steps.  ``decode_us_mean`` times the decode alone the same way,
+``unfused_us_per_step`` the two-launch step.  ``graph_us_per_step`` is the
+step replayed from a HIP graph.  ``decode_us_loops`` / ``decode_us_median``
+are five more loops of decode launches timed one by one; ``mall_resident`` is the
 decode reading one warm pool copy every launch; ``cache_line_efficiency`` is
-the decode's algorithmic bytes over the HBM bytes the counters measured (when
-they were taken on the current kernel sources).  ``prior_art`` times the
+the step's algorithmic bytes over the HBM bytes the counters measured on the
+step's launches (a ``--step-only`` run, on the current kernel sources).  ``prior_art`` times the
 pages' earlier design on the same GPU (gather the pages into dense tensors,
 then ordinary attention, in PyTorch).  ``cpu_baseline`` times the float64 CPU
 oracle on a bounded sample of the same batch, and again on one thread.
@@ -354,6 +358,9 @@ def main() -> int:
                     help="skip timing the step replayed from a HIP graph")
     ap.add_argument("--no-prior-art", action="store_true",
                     help="skip timing the gather-then-attention PyTorch baseline")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the steps only (no separate decode, write or graph timing), "
+                         "so that every decode-kernel launch is a fused step: for counter runs")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -413,9 +420,14 @@ def main() -> int:
                                   partition_size=ps, out=out, workspace=ws,
                                   counters=counters)
 
-    def step(i):
+    def unfused(i):
         write(i)
         decode(i)
+
+    def step(i):
+        r = i % R
+        pa.decode_step(q, key, value, kcs[r], vcs[r], tables, lens, scale,
+                       partition_size=ps, out=out, workspace=ws, counters=counters)
 
     def timed(fn, n, first):
         """Mean ms per call of n back-to-back calls, HIP events on `stream`."""
@@ -435,24 +447,29 @@ def main() -> int:
     ms_step = timed(step, args.steps, args.warmup)
     # Per-kernel means over K back-to-back launches of each kernel (no events
     # between launches, so the figures compare with a kernel trace).
-    k_mean_s = timed(decode, args.steps, args.warmup + args.steps) / 1e3
-    w_mean_s = timed(write, args.steps, args.warmup) / 1e3
-    # Spread: five more loops of decode launches, each timed on its own.
-    n_loop = max(20, args.steps // 5)
-    loops_us = [timed(decode, n_loop, j * n_loop) * 1e3 for j in range(5)]
-    # Warm single pool: every launch reads the same pool copy, which the
-    # 256 MB last-level cache can hold when the pool is smaller than it.
-    def decode_one_pool(i):
-        pa.paged_attention_decode(q, kc0, vc0, tables, lens, scale, partition_size=ps,
-                                  out=out, workspace=ws, counters=counters)
-    for i in range(3):
-        decode_one_pool(i)
-    warm_s = timed(decode_one_pool, args.steps, 0) / 1e3
+    k_mean_s = w_mean_s = unfused_ms = warm_s = None
+    loops_us = []
+    if not args.step_only:
+        k_mean_s = timed(decode, args.steps, args.warmup + args.steps) / 1e3
+        w_mean_s = timed(write, args.steps, args.warmup) / 1e3
+        unfused_ms = timed(unfused, args.steps, args.warmup)
+        # Spread: five more loops of decode launches, each timed on its own.
+        n_loop = max(20, args.steps // 5)
+        loops_us = [timed(decode, n_loop, j * n_loop) * 1e3 for j in range(5)]
+
+        # Warm single pool: every launch reads the same pool copy, which the
+        # 256 MB last-level cache can hold when the pool is smaller than it.
+        def decode_one_pool(i):
+            pa.paged_attention_decode(q, kc0, vc0, tables, lens, scale, partition_size=ps,
+                                      out=out, workspace=ws, counters=counters)
+        for i in range(3):
+            decode_one_pool(i)
+        warm_s = timed(decode_one_pool, args.steps, 0) / 1e3
 
     # The same steps replayed from a HIP graph (one graph holds one step per
     # pool copy); buffers were all allocated above, so capture allocates nothing.
     graph_us = None
-    if not args.no_graph:
+    if not args.no_graph and not args.step_only:
         graph = torch.cuda.CUDAGraph()
         torch.cuda.synchronize()
         with torch.cuda.graph(graph):
@@ -472,7 +489,7 @@ def main() -> int:
         del graph
 
     prior = None
-    if not args.no_prior_art:
+    if not args.no_prior_art and not args.step_only:
         n_pa = 20
         for i in range(3):
             gather_then_attention(q, kcs[i % R], vcs[i % R], tables, lens, scale)
@@ -487,10 +504,11 @@ def main() -> int:
             "decode_speedup": round(pa_ms / (k_mean_s * 1e3), 2),
         }
 
-    achieved = nbytes["decode"] / k_mean_s / 1e9
+    achieved = nbytes["step"] / (ms_step / 1e3) / 1e9
     traffic = None
     rec = traffic_record(w.name)
-    if rec and rec.get("workload") == w.name and rec.get("partition_size") == part:
+    if (rec and rec.get("workload") == w.name and rec.get("partition_size") == part
+            and rec.get("launch") == "fused step"):
         traffic = rec.get("hbm_bytes_per_launch")
     res = {
         "metric": METRIC,
@@ -511,16 +529,17 @@ def main() -> int:
             "sum_ctx": int(inp["context_lens"].sum()),
             "partition_size": part,
             "kv_pool_replicas": R,
-            "step": "reshape_and_cache + paged_attention_decode",
+            "step": "decode_step: the KV write of each new token fused into the decode launch",
         },
         "us_per_step": round(ms_step * 1e3, 3),
         "tokens_per_s": round(w.num_seqs / (ms_step / 1e3), 1),
-        "decode_us_mean": round(k_mean_s * 1e6, 3),
-        "write_us_mean": round(w_mean_s * 1e6, 3),
-        "decode_kv_gbs": round(nbytes["kv"] / k_mean_s / 1e9, 3),
+        "unfused_us_per_step": None if unfused_ms is None else round(unfused_ms * 1e3, 3),
+        "decode_us_mean": None if k_mean_s is None else round(k_mean_s * 1e6, 3),
+        "write_us_mean": None if w_mean_s is None else round(w_mean_s * 1e6, 3),
+        "decode_kv_gbs": None if k_mean_s is None else round(nbytes["kv"] / k_mean_s / 1e9, 3),
         "decode_us_loops": [round(x, 3) for x in loops_us],
-        "decode_us_median": round(float(np.median(loops_us)), 3),
-        "mall_resident": {
+        "decode_us_median": round(float(np.median(loops_us)), 3) if loops_us else None,
+        "mall_resident": None if warm_s is None else {
             "decode_us_mean": round(warm_s * 1e6, 3),
             "decode_gbs": round(nbytes["decode"] / warm_s / 1e9, 3),
             "pool_bytes": int(pool_bytes),
@@ -528,7 +547,7 @@ def main() -> int:
                     "when the pool fits the 256 MB last-level cache",
         },
         "cache_line_efficiency": (None if not traffic
-                                  else round(nbytes["decode"] / traffic, 4)),
+                                  else round(nbytes["step"] / traffic, 4)),
         "graph_us_per_step": None if graph_us is None else round(graph_us, 3),
         "roofline": {
             "bound": "hbm",
@@ -537,8 +556,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": decode_kernel_name(w),
-            "bytes_per_launch": nbytes["decode"],
+            "kernel": decode_kernel_name(w) + " (KV write fused)",
+            "bytes_per_launch": nbytes["step"],
         },
     }
     if prior is not None:

@@ -243,6 +243,35 @@ pa_status pa_paged_attention_decode(void* out, const void* q,
                                     pa_dtype dtype, void* stream);
 
 /*
+ * One decode step in one launch: the KV write of every sequence's new token
+ * (the write of the barellm README's paged-cache list: logical position ->
+ * block table -> physical slot) fused into the decode above.  In a decode
+ * step the new token of sequence b is the last of its L = context_lens[b]
+ * positions, so its rows go to
+ *     k_cache[block_tables[b, (L-1) / block_size], (L-1) % block_size, :, :] = key[b]
+ * and the same for V -- exactly what pa_reshape_and_cache does with that
+ * slot -- and the decode then reads them.  Out and caches are bit-identical
+ * to pa_reshape_and_cache (slot_mapping[b] = that slot) followed by
+ * pa_paged_attention_decode with the same arguments; this saves the write's
+ * launch.  Sequences with L == 0 or L past the table write nothing, nor does
+ * one whose slot names a block outside the pool.  The block that receives a
+ * sequence's new token must not be read by another sequence of the same call
+ * (a shared block is copied first: pa_copy_blocks).
+ *
+ *   key, value   [num_seqs, num_kv_heads, head_dim], 16-byte aligned (read)
+ *   k_cache, v_cache                                     (read and written)
+ *   every other argument as for pa_paged_attention_decode.
+ */
+pa_status pa_decode_step(void* out, const void* q, const void* key, const void* value,
+                         void* k_cache, void* v_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t num_blocks, int32_t block_size,
+                         int32_t max_blocks_per_seq, float scale, int32_t partition_size,
+                         void* workspace, size_t workspace_bytes, int32_t* counters,
+                         int64_t num_counters, pa_dtype dtype, void* stream);
+
+/*
  * Test and debugging aid: the exact gather a dense-attention engine would do
  * (barellm README, feature list: pages gathered into dense tensors).
  *

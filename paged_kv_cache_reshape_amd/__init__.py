@@ -9,6 +9,8 @@ Functions (names follow the C ABI in ``include/pagedattn.h``):
   reshape_and_cache(key, value, k_cache, v_cache, slot_mapping)
   paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens,
                          scale, partition_size=0, out=None, workspace=None)
+  decode_step(q, key, value, k_cache, v_cache, block_tables, context_lens,
+              scale, ...)   the write of each sequence's new token fused in
   decode_partition_size(...), decode_workspace_bytes(...)
   debug_gather_kv(k_cache, v_cache, block_tables, context_lens)
 """
@@ -22,7 +24,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "load_library", "PagedAttnError", "reshape_and_cache",
-    "paged_attention_decode", "decode_partition_size", "decode_workspace_bytes",
+    "paged_attention_decode", "decode_step", "decode_partition_size", "decode_workspace_bytes",
     "debug_gather_kv", "workspace_for", "counters_for",
 ]
 
@@ -74,6 +76,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.pa_paged_attention_decode.restype = i32
         lib.pa_paged_attention_decode.argtypes = [
             vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+            vp, sz, vp, i64, i32, vp]
+        lib.pa_decode_step.restype = i32
+        lib.pa_decode_step.argtypes = [
+            vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
             vp, sz, vp, i64, i32, vp]
         lib.pa_paged_attention_prefill.restype = i32
         lib.pa_paged_attention_prefill.argtypes = [
@@ -209,20 +215,13 @@ def counters_for(device: torch.device, count: int) -> torch.Tensor:
     return c
 
 
-def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                           block_tables: torch.Tensor, context_lens: torch.Tensor,
-                           scale: float, partition_size: int = 0,
-                           out: torch.Tensor | None = None,
-                           workspace: torch.Tensor | None = None,
-                           counters: torch.Tensor | None = None) -> torch.Tensor:
-    """Decode attention ``out[B, Hq, D]`` over the paged caches.
-
-    ``workspace`` (uint8, contents ignored) and ``counters`` (int32, all zero
-    before first use, kept zero by every call) default to per-stream buffers
-    managed here.
-    """
+def _decode_call(q, k_cache, v_cache, block_tables, context_lens, scale, partition_size,
+                 out, workspace, counters, step):
+    """Checks and buffers shared by the two decode entry points; `step` is
+    None or the (key, value) rows to write."""
     lib = load_library()
-    dev = _same_device(q, k_cache, v_cache, block_tables, context_lens)
+    extra = step if step is not None else ()
+    dev = _same_device(q, k_cache, v_cache, block_tables, context_lens, *extra)
     _need(q.dim() == 3, "q must be [B, Hq, D]")
     B, hq, d = q.shape
     _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape,
@@ -235,6 +234,11 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
           "context_lens must be int32 [B]")
     dt = _dtype_code(q)
     _need(k_cache.dtype == v_cache.dtype == q.dtype, "dtype mismatch")
+    if step is not None:
+        key, value = step
+        _need(key.shape == (B, hkv, d) and value.shape == key.shape,
+              "key/value must be [B, Hkv, D] matching q and the cache")
+        _need(key.dtype == value.dtype == q.dtype, "dtype mismatch")
     max_blocks = block_tables.shape[1]
     if out is None:
         out = torch.empty_like(q)
@@ -253,14 +257,50 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
               and counters.is_contiguous(), "counters must be contiguous int32 on the GPU")
     c_ptr = counters.data_ptr() if counters is not None else None
     c_len = counters.numel() if counters is not None else 0
-    with torch.cuda.device(dev):
-        st = lib.pa_paged_attention_decode(
-            out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-            block_tables.data_ptr(), context_lens.data_ptr(), B, hq, hkv, d, nb, bs,
+    tail = (block_tables.data_ptr(), context_lens.data_ptr(), B, hq, hkv, d, nb, bs,
             max_blocks, float(scale), partition_size, ws_ptr, ws_len, c_ptr, c_len, dt,
             _stream(dev))
-    _check(st, "pa_paged_attention_decode")
+    with torch.cuda.device(dev):
+        if step is None:
+            st = lib.pa_paged_attention_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
+                                               v_cache.data_ptr(), *tail)
+            what = "pa_paged_attention_decode"
+        else:
+            st = lib.pa_decode_step(out.data_ptr(), q.data_ptr(), key.data_ptr(),
+                                    value.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                    *tail)
+            what = "pa_decode_step"
+    _check(st, what)
     return out
+
+
+def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           scale: float, partition_size: int = 0,
+                           out: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None,
+                           counters: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention ``out[B, Hq, D]`` over the paged caches.
+
+    ``workspace`` (uint8, contents ignored) and ``counters`` (int32, all zero
+    before first use, kept zero by every call) default to per-stream buffers
+    managed here.
+    """
+    return _decode_call(q, k_cache, v_cache, block_tables, context_lens, scale, partition_size,
+                        out, workspace, counters, None)
+
+
+def decode_step(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                context_lens: torch.Tensor, scale: float, partition_size: int = 0,
+                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                counters: torch.Tensor | None = None) -> torch.Tensor:
+    """One decode step in one launch: each sequence's new rows ``key[b]`` /
+    ``value[b]`` (``[B, Hkv, D]``) are written at its position
+    ``context_lens[b] - 1``, then ``out[B, Hq, D]`` is computed as by
+    :func:`paged_attention_decode`."""
+    return _decode_call(q, k_cache, v_cache, block_tables, context_lens, scale, partition_size,
+                        out, workspace, counters, (key, value))
 
 
 def paged_attention_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

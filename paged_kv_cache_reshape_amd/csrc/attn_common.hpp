@@ -37,6 +37,11 @@ struct DecodeArgs {
   int32_t heads_per_wg;  // consecutive kv heads one workgroup takes (1, 2 or 4)
   int32_t deferred_merge;  // 1: partitions store their states and a second kernel merges
   float scale_log2;      // scale * log2(e): scores are kept in base-2 units
+  // Decode step with the KV write fused in: this step's token of sequence b
+  // ([num_seqs, num_kv_heads, D] rows), written at position ctx - 1 before
+  // the partition holding it is read.  nullptr: the caches are only read.
+  const void* new_k;
+  const void* new_v;
 };
 
 // Lane layout.  One KV row (one token, one kv head) is D*elt contiguous bytes
@@ -450,6 +455,36 @@ __device__ __forceinline__ bool partition_prologue(const DecodeArgs& a, int lane
   w.poisoned = __ballot(bad_here) != 0;  // same answer in every wave
   w.nblk_run = w.poisoned ? 0 : nblk;
   return true;
+}
+
+// Fused KV write of a decode step, by the workgroup of the partition that
+// holds position ctx - 1 (the step's token; called only there, uniformly):
+// the rows of its kv heads go from new_k / new_v to the cache slot the block
+// table gives for that position -- the slot a separate write would take --
+// unless that block lies outside the pool.  Only this workgroup reads those
+// rows in this launch; the barrier makes its stores visible to every wave's
+// loads that follow.
+template <class DT, int D, int BS, int NT>
+__device__ __forceinline__ void write_step_token(const DecodeArgs& a, const PartitionWork& w) {
+  using S = typename DT::storage;
+  const int pos = w.ctx - 1;
+  const int blk = w.block(pos / BS - w.blk0);
+  if (blk >= 0 && blk < a.num_blocks) {
+    constexpr int kChunk = DT::kPerChunk;  // elements per 16-byte chunk
+    const int hpw = a.heads_per_wg;
+    const int chunks = hpw * D / kChunk;  // per tensor
+    const size_t src = ((size_t)w.b * a.num_kv_heads + (size_t)w.gg * hpw) * D;
+    const size_t dst =
+        (((size_t)blk * BS + pos % BS) * a.num_kv_heads + (size_t)w.gg * hpw) * D;
+    for (int c = threadIdx.x; c < 2 * chunks; c += NT) {
+      const bool is_v = c >= chunks;
+      const size_t off = (size_t)(is_v ? c - chunks : c) * kChunk;
+      const S* from = static_cast<const S*>(is_v ? a.new_v : a.new_k) + src + off;
+      S* to = static_cast<S*>(const_cast<void*>(is_v ? a.v_cache : a.k_cache)) + dst + off;
+      store_chunk(to, load_chunk(from));
+    }
+  }
+  __syncthreads();
 }
 
 // End of a partition workgroup.  Every wave has left its state in LDS, one

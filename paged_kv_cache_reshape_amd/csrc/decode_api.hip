@@ -127,13 +127,17 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
   return p.total;
 }
 
-extern "C" pa_status pa_paged_attention_decode(
-    void* out, const void* q, const void* k_cache, const void* v_cache,
-    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
-    int32_t block_size, int32_t max_blocks_per_seq, float scale,
-    int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* counters,
-    int64_t num_counters, pa_dtype dtype, void* stream) {
+namespace {
+
+// Both decode entry points: with `step`, the step's token rows key / value
+// are written into the caches by the decode launch itself.
+pa_status decode_impl(void* out, const void* q, bool step, const void* key, const void* value,
+                      const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                      int32_t block_size, int32_t max_blocks_per_seq, float scale,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes,
+                      int32_t* counters, int64_t num_counters, pa_dtype dtype, void* stream) {
   clear_error();
   if (!supported_dtype(dtype)) {
     set_error("dtype %d is not PA_DTYPE_F32 or PA_DTYPE_BF16", (int)dtype);
@@ -194,6 +198,10 @@ extern "C" pa_status pa_paged_attention_decode(
     set_error("out, q, k_cache and v_cache must be 16-byte aligned");
     return PA_ERR_INVALID_ARGUMENT;
   }
+  if (step && (!key || !value || !aligned16(key) || !aligned16(value))) {
+    set_error("key and value must be non-NULL and 16-byte aligned");
+    return PA_ERR_INVALID_ARGUMENT;
+  }
   if (plan.total > 0) {
     if (workspace_bytes < plan.total) {
       set_error("workspace holds %zu bytes, needs %zu", workspace_bytes, plan.total);
@@ -234,6 +242,8 @@ extern "C" pa_status pa_paged_attention_decode(
   a.heads_per_wg = mfma ? 1 : plan.hpw;
   a.deferred_merge = plan.max_parts > 1 && deferred_merge(plan.max_parts);
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.new_k = step ? key : nullptr;
+  a.new_v = step ? value : nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t err = mfma ? launch_mfma(head_dim, block_size, G, a, s)
@@ -250,4 +260,32 @@ extern "C" pa_status pa_paged_attention_decode(
     }
   }
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" pa_status pa_paged_attention_decode(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+    int32_t block_size, int32_t max_blocks_per_seq, float scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* counters,
+    int64_t num_counters, pa_dtype dtype, void* stream) {
+  return decode_impl(out, q, false, nullptr, nullptr, k_cache, v_cache, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                     block_size, max_blocks_per_seq, scale, partition_size, workspace,
+                     workspace_bytes, counters, num_counters, dtype, stream);
+}
+
+extern "C" pa_status pa_decode_step(
+    void* out, const void* q, const void* key, const void* value, void* k_cache,
+    void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq, float scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* counters,
+    int64_t num_counters, pa_dtype dtype, void* stream) {
+  return decode_impl(out, q, true, key, value, k_cache, v_cache, block_tables, context_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                     max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes,
+                     counters, num_counters, dtype, stream);
 }

@@ -61,6 +61,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         st.load_q([&](int h) { return h < G ? q_grp + (size_t)h * D : nullptr; }, qs, lane);
       }))
     return;
+  if (a.new_k != nullptr && w.part == w.nparts - 1) write_step_token<BF16, D, BS, NT>(a, w);
   const int g = w.gg * hpw + hw;
   st.reset();
 

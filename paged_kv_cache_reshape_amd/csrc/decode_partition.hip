@@ -48,6 +48,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
                   col);
       }))
     return;
+  if (a.new_k != nullptr && w.part == w.nparts - 1) write_step_token<DT, D, BS, NT>(a, w);
   const int g = w.gg * hpw + hw;
   const int ctx = w.ctx, blk0 = w.blk0;
 

@@ -68,7 +68,7 @@ def _per_dispatch(counter_csv: str, counter: str) -> dict:
 
 
 def traffic_record(fetch_csv: str, write_csv: str, workload: str, partition_size: int,
-                   command: str) -> dict:
+                   command: str, fused_step: bool = False) -> dict:
     import numpy as np
 
     import bench
@@ -86,12 +86,15 @@ def traffic_record(fetch_csv: str, write_csv: str, workload: str, partition_size
     write_factor = k_cache_bytes / 1024.0 / write[copy_key]
     read_b = fetch["decode"] * fetch_factor * 1024.0
     write_b = write["decode"] * write_factor * 1024.0
-    inp_bytes = bench.algorithmic_bytes(synth.make_inputs(w))["decode"]
+    # Counters of a `bench.py --step-only` run see only the fused step's
+    # launches (decode with the KV write in it): their algorithmic bytes.
+    inp_bytes = bench.algorithmic_bytes(synth.make_inputs(w))["step" if fused_step else "decode"]
     out_json = bench.traffic_file(workload)
     rec = {
         "workload": workload,
         "partition_size": partition_size,
         "kernel": bench.decode_kernel_name(w),
+        "launch": "fused step" if fused_step else "decode",
         "command": command,
         "fetch_size_kib_per_dispatch": round(fetch["decode"], 2),
         "write_size_kib_per_dispatch": round(write["decode"], 2),
@@ -111,7 +114,8 @@ def traffic_record(fetch_csv: str, write_csv: str, workload: str, partition_size
     md = os.path.splitext(out_json)[0] + ".md"
     open(md, "w").write(
         f"# HBM traffic of {rec['kernel']}\n\n"
-        f"Workload `{workload}`, partition size {partition_size}.\n\n"
+        f"Workload `{workload}`, partition size {partition_size}; "
+        f"{'launches of the fused step (the KV write inside the decode)' if fused_step else 'decode launches'}.\n\n"
         "Commands (one counter per run):\n\n```\n" + command + "\n```\n\n"
         "| | FETCH_SIZE (KiB/dispatch) | WRITE_SIZE (KiB/dispatch) |\n|---|---|---|\n"
         f"| copy kernel, {k_cache_bytes} B known | {fetch[copy_key]:.1f} | {write[copy_key]:.1f} |\n"
@@ -155,6 +159,8 @@ def main(argv=None) -> int:
     f.add_argument("--workload", default="qwen3_0p6b")
     f.add_argument("--partition-size", type=int, required=True)
     f.add_argument("--command", required=True)
+    f.add_argument("--fused-step", action="store_true",
+                   help="the counters come from `bench.py --step-only` (fused-step launches)")
     c = sub.add_parser("counters")
     c.add_argument("out_md")
     c.add_argument("csvs", nargs="+")
@@ -167,7 +173,7 @@ def main(argv=None) -> int:
         print(json.dumps(counters_summary(a.csvs, a.kernel, a.out_md, a.command), indent=1))
     else:
         print(json.dumps(traffic_record(a.fetch_csv, a.write_csv, a.workload,
-                                        a.partition_size, a.command), indent=1))
+                                        a.partition_size, a.command, a.fused_step), indent=1))
     return 0
 
 

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("pa_reshape_and_cache", "pa_paged_attention_decode",
+    for n in ("pa_reshape_and_cache", "pa_paged_attention_decode", "pa_decode_step",
               "pa_decode_workspace_bytes", "pa_decode_partition_size",
               "pa_debug_gather_kv", "pa_status_string", "pa_last_error_message",
               "pa_version"):
@@ -81,6 +81,31 @@ def _decode(lib, **kw):
 ])
 def test_decode_argument_checks(lib, kw, status):
     assert _decode(lib, **kw) == status
+    if status:
+        assert lib.pa_last_error_message() != b""
+
+
+def _step(lib, **kw):
+    a = dict(out=16, q=16, key=16, value=16, k=16, v=16, bt=16, cl=16, B=4, Hq=4, Hkv=2, D=64,
+             nb=32, bs=16, mb=4, scale=0.125, ps=0, ws=None, wsb=0, cnt=None, ncnt=0, dt=0)
+    a.update(kw)
+    return lib.pa_decode_step(
+        a["out"], a["q"], a["key"], a["value"], a["k"], a["v"], a["bt"], a["cl"], a["B"],
+        a["Hq"], a["Hkv"], a["D"], a["nb"], a["bs"], a["mb"], a["scale"], a["ps"], a["ws"],
+        a["wsb"], a["cnt"], a["ncnt"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(key=None), INVALID),
+    (dict(value=None), INVALID),
+    (dict(key=24), INVALID),                # misaligned
+    (dict(dt=5), INVALID),                  # the decode's own checks come first
+    (dict(Hq=12, Hkv=4), UNSUPPORTED),
+    (dict(mb=400, ps=16), WS_SMALL),
+    (dict(B=0, q=None, out=None, key=None, value=None), OK),  # empty batch
+])
+def test_decode_step_argument_checks(lib, kw, status):
+    assert _step(lib, **kw) == status
     if status:
         assert lib.pa_last_error_message() != b""
 

@@ -373,6 +373,64 @@ def test_bad_table_entries_give_nan_rows_only(name, ps, merge, monkeypatch):
     assert np.array_equal(G.host_storage(out)[keep], base[keep])
 
 
+# ------------------------------------------------------------------ fused step
+def fused_step(d, partition_size=0):
+    return pa.decode_step(d["q"], d["key"], d["value"], d["k_cache"], d["v_cache"],
+                          d["block_tables"], d["context_lens"], d["scale"],
+                          partition_size=partition_size)
+
+
+@pytest.mark.parametrize("name,ps", [("qwen3_0p6b", 0), ("qwen3_0p6b", 64), ("tiny_f32", 0),
+                                     ("llama32_1b", 0), ("mqa_large", 0),
+                                     ("bf16_d128_bs16_g16", 128), ("bf16_d128_bs16_g16", 32),
+                                     ("bf16_d64_bs32_g8", 0), ("f32_d128_bs32_g4", 64)])
+def test_decode_step_equals_write_then_decode(name, ps):
+    """The fused step (write of each sequence's token at position L - 1 inside
+    the decode launch) gives the bits of the two calls: the output and both
+    caches, in both kernels and with either merge path."""
+    inp = inputs_for(name)
+    say("fused step", name, ps)
+    d1, d2 = G.upload(inp), G.upload(inp)
+    want = G.host_storage(gpu_step(d1, ps))
+    got = G.host_storage(fused_step(d2, ps))
+    assert np.array_equal(got, want)
+    for c in ("k_cache", "v_cache"):
+        assert torch.equal(d1[c], d2[c]), c
+
+
+def test_decode_step_edge_sequences():
+    """Empty sequences, a new token whose block lies outside the pool and a
+    length past the table write nothing; their rows are what the decode
+    gives (zeros, NaN), every other row and slot is the two calls' result;
+    a sequence of one token sees only the token just written."""
+    w = synth.WORKLOADS["qwen3_0p6b"]
+    ctx = G.cached_inputs("qwen3_0p6b")["context_lens"].copy()
+    ctx[[0, 5]] = 0
+    ctx[9] = 1
+    inp = synth.make_inputs(w, context_lens=ctx)
+    t = inp["block_tables"].copy()
+    c = inp["context_lens"].copy()
+    t[7, (c[7] - 1) // 16] = inp["num_blocks"] + 3   # the new token's block: outside the pool
+    c[11] = (t.shape[1] + 1) * 16                    # past the table
+    slots = inp["slot_mapping"].copy()
+    slots[[7, 11]] = -1                              # what the fused step writes for them
+    say("fused step edge sequences")
+    d1, d2 = G.upload(inp), G.upload(inp)
+    for d in (d1, d2):
+        d["block_tables"] = torch.from_numpy(t).cuda()
+        d["context_lens"] = torch.from_numpy(c).cuda()
+    d1["slot_mapping"] = torch.from_numpy(slots).cuda()
+    want = G.host_storage(gpu_step(d1, 256))
+    got_dev = fused_step(d2, 256)
+    assert np.array_equal(G.host_storage(got_dev), want)
+    for name in ("k_cache", "v_cache"):
+        assert torch.equal(d1[name], d2[name]), name
+    got = G.host_f64(got_dev)
+    assert np.all(got[[0, 5]] == 0) and np.all(np.isnan(got[[7, 11]]))
+    ref, _ = oracle_step(inp, seqs=[9])
+    G.assert_close(got[[9]], ref, "bf16", "one-token sequence")
+
+
 def test_side_stream_and_given_out():
     """Work goes on the caller's current stream; `out` may be supplied."""
     inp = inputs_for("qwen3_0p6b")
@@ -470,18 +528,20 @@ def test_prefix_fork_copy_on_write():
 
 
 # ------------------------------------------------------------------ graph capture
-@pytest.mark.parametrize("name,ps", [("qwen3_0p6b", None), ("mqa_large", None),
-                                     ("qwen3_0p6b", 64)])
-def test_graph_replays_match_eager(name, ps):
-    """A step (KV write + decode) captured in a HIP graph: every replay, with
-    eager launches and host synchronisations between replays, gives the eager
-    result bit for bit.  The workspace and the arrival counters are allocated
-    before capture and passed in, so nothing is allocated or cleared inside
-    the graph (the kernels leave the counters at zero themselves).  At 64-token
-    partitions the step holds the separate merge kernel too."""
+@pytest.mark.parametrize("name,ps,fused", [("qwen3_0p6b", None, False), ("mqa_large", None, False),
+                                           ("qwen3_0p6b", 64, False), ("qwen3_0p6b", None, True),
+                                           ("qwen3_0p6b", 64, True)])
+def test_graph_replays_match_eager(name, ps, fused):
+    """A step (KV write + decode, or the fused step) captured in a HIP graph:
+    every replay, with eager launches and host synchronisations between
+    replays, gives the eager result bit for bit.  The workspace and the
+    arrival counters are allocated before capture and passed in, so nothing
+    is allocated or cleared inside the graph (the kernels leave the counters
+    at zero themselves).  At 64-token partitions the step holds the separate
+    merge kernel too."""
     inp = inputs_for(name)
     w = inp["workload"]
-    say("graph capture", name, ps)
+    say("graph capture", name, ps, "fused" if fused else "")
     d = G.upload(inp)
     B, hq, hkv = w.num_seqs, w.num_q_heads, w.num_kv_heads
     mb = d["block_tables"].shape[1]
@@ -491,6 +551,11 @@ def test_graph_replays_match_eager(name, ps):
     cnt = torch.zeros(B * hkv, dtype=torch.int32, device="cuda")
 
     def step(out):
+        if fused:
+            pa.decode_step(d["q"], d["key"], d["value"], d["k_cache"], d["v_cache"],
+                           d["block_tables"], d["context_lens"], d["scale"], partition_size=ps,
+                           out=out, workspace=ws, counters=cnt)
+            return
         pa.reshape_and_cache(d["key"], d["value"], d["k_cache"], d["v_cache"],
                              d["slot_mapping"])
         pa.paged_attention_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
