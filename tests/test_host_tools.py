@@ -1,0 +1,72 @@
+"""Host-side tools of the benchmark, checked without a GPU: the algorithmic
+byte counts the roofline divides by, and the HBM-traffic record built from
+rocprofv3 counter files (scaled by a copy kernel of known size)."""
+import csv
+import json
+
+import numpy as np
+import pytest
+
+import bench
+import synth
+from paged_kv_cache_reshape_amd import profiling
+
+
+def test_algorithmic_bytes_of_the_tiny_batch():
+    """Worked by hand: contexts {1, 17, 33, 64} (115 tokens), B=4, Hq=4,
+    Hkv=2, D=64, 4-byte elements, 16-token blocks."""
+    nb = bench.algorithmic_bytes(synth.make_inputs(synth.WORKLOADS["tiny_f32"]))
+    assert nb["kv"] == 115 * 2 * 2 * 64 * 4 == 117_760      # K and V rows read once
+    q_and_out = 2 * 4 * 4 * 64 * 4                          # q read, out written
+    table = (1 + 2 + 3 + 4) * 4 + 4 * 4                     # used entries + lengths
+    assert nb["decode"] == nb["kv"] + q_and_out + table
+    write = 2 * 2 * 4 * 2 * 64 * 4 + 8 * 4                  # 4 new K/V rows in and out, slots
+    assert nb["write"] == write
+    assert nb["step"] == nb["decode"] + nb["write"]
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value",
+                                           "Grid_Size"])
+        wr.writeheader()
+        for name, value, grid in rows:
+            wr.writerow(dict(Kernel_Name=name, Counter_Name=counter, Counter_Value=value,
+                             Grid_Size=grid))
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_traffic_record_is_scaled_by_the_copy_kernel(tmp_path, monkeypatch, fused):
+    """The biggest copy kernel clones one K pool (size known): its counter
+    readings fix the scale of each counter; the decode kernel's mean reading
+    per dispatch, so scaled, is the record's HBM bytes per launch, set
+    against the step's algorithmic bytes for fused-step counter runs and the
+    decode's otherwise."""
+    wl = "tiny_f32"
+    w = synth.WORKLOADS[wl]
+    ctx = synth.draw_context_lens(w, np.random.default_rng(w.seed))
+    k_bytes = (synth.pool_blocks(w, ctx) * w.block_size * w.num_kv_heads * w.head_dim *
+               w.elt_bytes)
+    dec = "void pa::decode_partition_kernel<pa::F32, 64, 16, 2, 4>(pa::DecodeArgs)"
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    # FETCH_SIZE reads half of what the copy moved, WRITE_SIZE all of it (KiB).
+    _counter_csv(fetch, "FETCH_SIZE", [("__amd_rocclr_copyBuffer", k_bytes / 2048, 999),
+                                       ("__amd_rocclr_copyBuffer", 1.0, 3),
+                                       (dec, 100.0, 64), (dec, 140.0, 64)])
+    _counter_csv(write, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", k_bytes / 1024, 999),
+                                       ("__amd_rocclr_copyBuffer", 1.0, 3),
+                                       (dec, 2.0, 64), (dec, 4.0, 64)])
+    monkeypatch.setattr(bench, "traffic_file",
+                        lambda workload: str(tmp_path / f"traffic_{workload}.json"))
+    rec = profiling.traffic_record(str(fetch), str(write), wl, 512, "the commands", fused)
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["hbm_read_bytes_per_launch"] == 120 * 2 * 1024
+    assert rec["hbm_write_bytes_per_launch"] == 3 * 1024
+    nb = bench.algorithmic_bytes(synth.make_inputs(w))
+    assert rec["algorithmic_bytes_per_launch"] == nb["step" if fused else "decode"]
+    assert rec["launch"] == ("fused step" if fused else "decode")
+    # Written where the benchmark looks, under the current source hash, so
+    # the benchmark takes it; another hash makes it stale.
+    assert bench.traffic_record(wl) == json.load(open(tmp_path / f"traffic_{wl}.json"))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
+    assert bench.traffic_record(wl) is None
