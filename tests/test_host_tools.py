@@ -3,6 +3,9 @@ byte counts the roofline divides by, and the HBM-traffic record built from
 rocprofv3 counter files (scaled by a copy kernel of known size)."""
 import csv
 import json
+import os
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -70,3 +73,12 @@ def test_traffic_record_is_scaled_by_the_copy_kernel(tmp_path, monkeypatch, fuse
     assert bench.traffic_record(wl) == json.load(open(tmp_path / f"traffic_{wl}.json"))
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
     assert bench.traffic_record(wl) is None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """One GPU only: with --gpus 2 the benchmark says so and exits with 2."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
