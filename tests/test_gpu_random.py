@@ -3,7 +3,8 @@ oracle, through the C ABI, on combinations the fixed shapes do not reach.
 
 Each case draws, from its own seed, the element type, head size, block size,
 query heads per kv head, kv heads, batch size, the spread of context lengths
-(empty sequences included) and the partition size (or the library's choice);
+(empty sequences included) and the partition size (or the library's choice),
+and checks the fused step against the write + decode calls bit for bit;
 for the prefill, whole prompts or chunks and the key-halves form.  The bar is
 the one of the other parity tests: bf16 2e-3 + 1e-2|y|, f32 1e-5 + 1e-5|y|.
 """
@@ -59,6 +60,13 @@ def test_random_decode_shapes(seed, monkeypatch):
     ref = oracle.decode(inp["q"], k, v, inp["block_tables"], inp["context_lens"],
                         inp["scale"], w.dtype)
     G.assert_close(G.host_f64(out), ref, w.dtype, f"random decode {seed}")
+    # The fused step on fresh caches: the same bits, output and caches.
+    d2 = G.upload(inp)
+    out2 = pa.decode_step(d2["q"], d2["key"], d2["value"], d2["k_cache"], d2["v_cache"],
+                          d2["block_tables"], d2["context_lens"], d2["scale"],
+                          partition_size=part)
+    assert np.array_equal(G.host_storage(out2), G.host_storage(out))
+    assert torch.equal(d2["k_cache"], d["k_cache"]) and torch.equal(d2["v_cache"], d["v_cache"])
 
 
 def prefill_case(seed: int):
