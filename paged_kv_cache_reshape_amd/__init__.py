@@ -1,4 +1,4 @@
-"""Python binding of libpagedattn (paged KV write + paged decode attention).
+"""Python binding of libpagedattn (paged KV write, decode and prefill attention).
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libpagedattn.so``.  PyTorch supplies device memory and the
@@ -11,6 +11,9 @@ Functions (names follow the C ABI in ``include/pagedattn.h``):
                          scale, partition_size=0, out=None, workspace=None)
   decode_step(q, key, value, k_cache, v_cache, block_tables, context_lens,
               scale, ...)   the write of each sequence's new token fused in
+  paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens,
+                          query_start, scale, max_query_len=None, out=None)
+  copy_blocks(k_cache, v_cache, block_pairs)
   decode_partition_size(...), decode_workspace_bytes(...)
   debug_gather_kv(k_cache, v_cache, block_tables, context_lens)
 """
@@ -24,8 +27,9 @@ import torch
 
 __all__ = [
     "LIB_PATH", "load_library", "PagedAttnError", "reshape_and_cache",
-    "paged_attention_decode", "decode_step", "decode_partition_size", "decode_workspace_bytes",
-    "debug_gather_kv", "workspace_for", "counters_for",
+    "paged_attention_decode", "decode_step", "paged_attention_prefill", "copy_blocks",
+    "decode_partition_size", "decode_workspace_bytes", "debug_gather_kv", "workspace_for",
+    "counters_for",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
