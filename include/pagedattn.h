@@ -23,8 +23,9 @@
  * Conventions for every call:
  *   - All tensors are dense, row-major, in device memory, 16-byte aligned,
  *     and owned by the caller.  The library never allocates, frees or
- *     synchronises; it keeps no state between calls except a per-device
- *     cache of the compute-unit count.
+ *     synchronises; it keeps no state between calls except each host
+ *     thread's last error message (the decode's arrival counters are the
+ *     caller's, left at zero by every call).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     runs asynchronously; results are visible after the caller synchronises.
  *   - Arguments are checked before anything is launched.  On failure the call
