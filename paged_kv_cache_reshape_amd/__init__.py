@@ -19,7 +19,9 @@ Functions (names follow the C ABI in ``include/pagedattn.h``):
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 import os
 import threading
 
@@ -122,6 +124,14 @@ def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _on(device: torch.device):
+    """Make `device` current for the call (a no-op context when it already
+    is: entering torch.cuda.device costs more than a launch on small batches)."""
+    if device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
+
+
 def _same_device(*ts: torch.Tensor) -> torch.device:
     dev = ts[0].device
     _need(dev.type == "cuda", "tensors must be on a GPU")
@@ -145,7 +155,7 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Ten
           "slot_mapping must be int64 [N]")
     dt = _dtype_code(k_cache)
     _need(key.dtype == value.dtype == v_cache.dtype == k_cache.dtype, "dtype mismatch")
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib.pa_reshape_and_cache(
             key.data_ptr(), value.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             slot_mapping.data_ptr(), key.shape[0], hkv, d, nb, bs, dt, _stream(dev))
@@ -167,7 +177,7 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
     nb, bs, hkv, d = k_cache.shape
     dt = _dtype_code(k_cache)
     _need(v_cache.dtype == k_cache.dtype, "dtype mismatch")
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib.pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), block_pairs.data_ptr(),
                                 block_pairs.shape[0], hkv, d, nb, bs, dt, _stream(dev))
     _check(st, "pa_copy_blocks")
@@ -180,6 +190,7 @@ def decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
         requested))
 
 
+@functools.lru_cache(maxsize=256)
 def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                            max_blocks_per_seq, block_size, partition_size=0) -> int:
     return int(load_library().pa_decode_workspace_bytes(
@@ -191,7 +202,8 @@ _workspaces: dict = {}
 _counters: dict = {}
 
 
-def workspace_for(device: torch.device, nbytes: int) -> torch.Tensor | None:
+def workspace_for(device: torch.device, nbytes: int,
+                  stream: int | None = None) -> torch.Tensor | None:
     """A workspace of >= nbytes for this device and current stream (cached).
 
     Its contents need no initialisation; it is reused by later calls on the
@@ -199,7 +211,7 @@ def workspace_for(device: torch.device, nbytes: int) -> torch.Tensor | None:
     """
     if nbytes == 0:
         return None
-    key = (device.index, _stream(device))
+    key = (device.index, _stream(device) if stream is None else stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -207,11 +219,11 @@ def workspace_for(device: torch.device, nbytes: int) -> torch.Tensor | None:
     return ws
 
 
-def counters_for(device: torch.device, count: int) -> torch.Tensor:
+def counters_for(device: torch.device, count: int, stream: int | None = None) -> torch.Tensor:
     """Zero-initialised int32 arrival counters (>= count) for this device and
     current stream.  Every decode call leaves the counters it used at zero, so
     one array serves all later calls on the stream, whatever their sizes."""
-    key = (device.index, _stream(device))
+    key = (device.index, _stream(device) if stream is None else stream)
     c = _counters.get(key)
     if c is None or c.numel() < count:
         c = torch.zeros(max(count, 1024), dtype=torch.int32, device=device)
@@ -250,12 +262,13 @@ def _decode_call(q, k_cache, v_cache, block_tables, context_lens, scale, partiti
         _same_device(out)
         _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     need = decode_workspace_bytes(B, hq, hkv, d, max_blocks, bs, partition_size)
+    stream = _stream(dev)
     if workspace is None:
-        workspace = workspace_for(dev, need)
+        workspace = workspace_for(dev, need, stream)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if need and counters is None:
-        counters = counters_for(dev, B * hkv)
+        counters = counters_for(dev, B * hkv, stream)
     if counters is not None:
         _need(counters.dtype == torch.int32 and counters.device == dev
               and counters.is_contiguous(), "counters must be contiguous int32 on the GPU")
@@ -263,8 +276,8 @@ def _decode_call(q, k_cache, v_cache, block_tables, context_lens, scale, partiti
     c_len = counters.numel() if counters is not None else 0
     tail = (block_tables.data_ptr(), context_lens.data_ptr(), B, hq, hkv, d, nb, bs,
             max_blocks, float(scale), partition_size, ws_ptr, ws_len, c_ptr, c_len, dt,
-            _stream(dev))
-    with torch.cuda.device(dev):
+            stream)
+    with _on(dev):
         if step is None:
             st = lib.pa_paged_attention_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
                                                v_cache.data_ptr(), *tail)
@@ -344,7 +357,7 @@ def paged_attention_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
     else:
         _same_device(out)
         _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib.pa_paged_attention_prefill(
             out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             block_tables.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(), B, T,
@@ -366,7 +379,7 @@ def debug_gather_kv(k_cache: torch.Tensor, v_cache: torch.Tensor,
     dt = _dtype_code(k_cache)
     kd = torch.empty((B, max_blocks * bs, hkv, d), dtype=k_cache.dtype, device=dev)
     vd = torch.empty_like(kd)
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib.pa_debug_gather_kv(
             kd.data_ptr(), vd.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             block_tables.data_ptr(), context_lens.data_ptr(), B, hkv, d, nb, bs,
