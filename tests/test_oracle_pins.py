@@ -1,4 +1,6 @@
 """The CPU oracle against facts that do not come from the oracle (CPU only)."""
+import os
+
 import numpy as np
 import pytest
 
@@ -75,6 +77,35 @@ def test_widen_matches_torch_bf16():
 
 
 # ------------------------------------------------------------ pins
+
+def _golden_rows(name):
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)
+    rows = [line.split() for line in open(path) if line.strip() and not line.startswith("#")]
+    return [tuple(int(v) for v in r) for r in rows]
+
+
+def test_golden_tiny_newest_token():
+    """The tiny batch's newest tokens, worked by hand from the paged-cache
+    definition (tests/golden/tiny_newest_token.txt): the generator's slots, the
+    oracle's write and the oracle's gather all put each new row there."""
+    rows = _golden_rows("tiny_newest_token.txt")
+    x = synth.make_inputs(W1)
+    bs = W1.block_size
+    assert [r[0] for r in rows] == [int(c) for c in x["context_lens"]]
+    k2, v2 = oracle.reshape_and_cache(x["key"], x["value"], x["k_cache"], x["v_cache"],
+                                      x["slot_mapping"])
+    kd = oracle.gather_kv(k2, x["block_tables"], x["context_lens"])
+    vd = oracle.gather_kv(v2, x["block_tables"], x["context_lens"])
+    kd0 = oracle.gather_kv(x["k_cache"], x["block_tables"], x["context_lens"])
+    for b, (ctx, pos, lblk, off, used) in enumerate(rows):
+        table = x["block_tables"][b]
+        assert int((table >= 0).sum()) == used
+        assert int(x["slot_mapping"][b]) == int(table[lblk]) * bs + off
+        assert np.array_equal(kd[b, pos].view(np.uint8), x["key"][b].view(np.uint8))
+        assert np.array_equal(vd[b, pos].view(np.uint8), x["value"][b].view(np.uint8))
+        # every earlier row of the sequence is untouched by the write
+        assert np.array_equal(kd[b, :pos].view(np.uint8), kd0[b, :pos].view(np.uint8))
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_p1_write_slots(name):
     inp = synth.make_inputs(SMALL[name])
