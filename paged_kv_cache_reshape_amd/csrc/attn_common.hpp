@@ -287,12 +287,13 @@ __device__ __forceinline__ void stream_blocks(int first, int step, int n, Fetch&
   }
 }
 
-// Merge stored partial states (m, l, acc) of one group of query heads into the
-// output.  `piece_rows(i)` returns the row index (into ws_ml / 2 and ws_acc /
-// D) of the first query head of piece i; rows of one piece are consecutive.
-// Pieces are read in index order through LDS in chunks of 64, so the result
-// does not depend on the order in which they were written.  Used by one whole
-// workgroup; `gh` query heads, D values each, output at out + out_base.
+// Merge stored partial states (m, l, acc) of `gh` output rows into the
+// output.  `row_of(p, r)` returns the row index (into ws_ml / 2 and ws_acc /
+// D) of output row r in piece p, so the rows of several kv heads, which lie
+// apart in the workspace, merge in one pass.  Pieces are read in index order
+// through LDS in chunks of 64, so the result does not depend on the order in
+// which they were written.  Used by one whole workgroup; `gh` rows of D values
+// each, output at out + out_base (rows consecutive).
 //
 // The partial outputs are read with system-scope loads, which go to memory:
 // every thread first issues the loads of U pieces for all its output
@@ -300,7 +301,7 @@ __device__ __forceinline__ void stream_blocks(int first, int step, int n, Fetch&
 // in flight per thread instead of one round trip per value.
 template <class DT, int D, int GH, int NT, int kInFlight = 16, class RowFn>
 __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int npieces, int gh,
-                                             RowFn piece_rows, size_t out_base,
+                                             RowFn row_of, size_t out_base,
                                              float (*s_pm)[GH], float (*s_pl)[GH]) {
   constexpr int kChunk = 64;
   constexpr int EPT = (GH * D + NT - 1) / NT;  // output elements per thread, at most
@@ -323,9 +324,9 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int npieces, i
   auto load_batch = [&](int c0, int p0, int n) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const size_t row = piece_rows(c0 + min(p0 + u, n - 1));
+      const int pc = c0 + min(p0 + u, n - 1);
 #pragma unroll
-      for (int k = 0; k < EPT; ++k) v[u][k] = collect(a.ws_acc + (row + qh[k]) * D + dd[k]);
+      for (int k = 0; k < EPT; ++k) v[u][k] = collect(a.ws_acc + row_of(pc, qh[k]) * D + dd[k]);
     }
   };
   for (int c0 = 0; c0 < npieces; c0 += kChunk) {
@@ -335,7 +336,7 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int npieces, i
     load_batch(c0, 0, n);
     for (int i = tid; i < n * gh; i += NT) {
       const int pp = i / gh, h = i % gh;
-      const size_t r = piece_rows(c0 + pp) + h;
+      const size_t r = row_of(c0 + pp, h);
       s_pm[pp][h] = collect(a.ws_ml + r * 2);
       s_pl[pp][h] = collect(a.ws_ml + r * 2 + 1);
     }
@@ -494,7 +495,7 @@ __device__ __forceinline__ void write_step_token(const DecodeArgs& a, const Part
 // sequence fits one partition), or the partial state is published and the
 // last workgroup of the (sequence, head group) to arrive merges every
 // partition into the output.
-template <class DT, int D, int G, int GW, int HS, int NW>
+template <class DT, int D, int G, int GW, int HS, int NW, int HPW>
 __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int gg, int part,
                                                  int nparts, bool poisoned,
                                                  const float (*s_acc)[GW][D],
@@ -519,11 +520,13 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
   // Qwen3 batch 33.8 -> 34.1 us when shared).  Same operations in the same
   // order either way, so the results are the same bits.  The shared factors
   // live in the merge's LDS area, not used before the combine is over:
-  // nwt * rows = NW * GW factors fit in s_pm, 2 * rows in s_pl.
+  // nwt * rows = NW * GW factors fit in s_pm, 2 * rows in s_pl.  HPW is the
+  // most kv heads a workgroup takes, so kRows bounds its output rows.
   constexpr bool kRowFactors = G >= 8;
-  static_assert(NW * GW <= 64 * G, "combine factors must fit the merge's LDS area");
-  __shared__ float s_pm[64][G];
-  __shared__ float s_pl[64][G];
+  constexpr int kRows = HPW * G;
+  static_assert(NW * GW <= 64 * kRows, "combine factors must fit the merge's LDS area");
+  __shared__ float s_pm[64][kRows];
+  __shared__ float s_pl[64][kRows];
   const int rows = hpw * G;
   float* s_fac = &s_pm[0][0];  // [t][r]: t * rows + r
   float* s_rm = &s_pl[0][0];
@@ -596,16 +599,31 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
   int32_t* counter = a.counters + (size_t)b * n_groups + gg;
   if (!arrive(counter, nparts, &s_last)) return;
 
-  // Rows of partition p for query head qh of kv head x of the group: pieces
-  // of one kv head are max_parts * G rows apart, so merge one kv head at a
-  // time.
+  // Output row r of the group is query head r % G of kv head r / G; the
+  // pieces of one kv head are max_parts * G rows apart.  All the group's rows
+  // merge in one pass (one round trip for every kv head's states), sized for
+  // the group's own number of kv heads, so that each thread's loads cover as
+  // many pieces as they can.
   const size_t head_rows = (size_t)a.max_parts * G;
   const size_t grp_base = ((size_t)b * Hkv + (size_t)gg * hpw) * head_rows;
-  for (int x = 0; x < hpw; ++x) {
-    const size_t base = grp_base + x * head_rows;
-    merge_pieces<DT, D, G, NT>(
-        a, nparts, G, [&](int p) { return base + (size_t)p * G; },
-        out_base + (size_t)x * G * D, s_pm, s_pl);
+  const auto row_of = [&](int p, int r) {
+    return grp_base + (size_t)(r / G) * head_rows + (size_t)p * G + r % G;
+  };
+  const auto merge = [&](auto gh) {
+    constexpr int GH = decltype(gh)::value;
+    merge_pieces<DT, D, GH, NT>(a, nparts, rows, row_of, out_base,
+                                reinterpret_cast<float (*)[GH]>(&s_pm[0][0]),
+                                reinterpret_cast<float (*)[GH]>(&s_pl[0][0]));
+  };
+  if (hpw == 1) {
+    merge(IntC<G>{});
+  } else {
+    if constexpr (HPW >= 2) {
+      if (hpw == 2)
+        merge(IntC<2 * G>{});
+      else
+        merge(IntC<kRows>{});
+    }
   }
   reset_counter(counter);
 }
@@ -631,7 +649,8 @@ __device__ __forceinline__ void merge_partitions(const DecodeArgs& a, int bs) {
   // Nothing else runs in this kernel: its registers take a whole chunk of
   // pieces in one round trip.
   merge_pieces<DT, D, G, NT, 64>(
-      a, nparts, G, [&](int p) { return base + (size_t)p * G; }, out_base, s_pm, s_pl);
+      a, nparts, G, [&](int p, int r) { return base + (size_t)p * G + r; }, out_base, s_pm,
+      s_pl);
 }
 
 }  // namespace pa

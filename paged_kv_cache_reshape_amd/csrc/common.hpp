@@ -10,6 +10,12 @@
 
 namespace pa {
 
+// A compile-time int carried by a value (template dispatch over shapes).
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
 // ------------------------------------------------------------------ storage
 // A "chunk" is the 16 bytes one lane moves with one 128-bit load or store.
 struct F32 {

@@ -11,11 +11,6 @@ namespace pa {
 #endif
 constexpr int kDecodeWaves = PA_DECODE_WAVES;  // waves per workgroup
 
-template <int V>
-struct IntC {
-  static constexpr int value = V;
-};
-
 // Calls f(dtype_tag, IntC<D>, IntC<BS>, IntC<G>) for the built combination.
 template <class F>
 hipError_t dispatch_decode(int dtype, int D, int BS, int G, F&& f) {

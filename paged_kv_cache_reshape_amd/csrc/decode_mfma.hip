@@ -125,8 +125,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   float(*s_l)[G] = reinterpret_cast<float(*)[G]>(s_raw + NW * G * (D + 1) * 4);
   st.to_lds(s_acc[wave], s_m[wave], s_l[wave], lane);
   __syncthreads();
-  finish_partition<BF16, D, G, G, 1, NW>(a, w.b, w.gg, w.part, w.nparts, w.poisoned, s_acc,
-                                            s_m, s_l);
+  finish_partition<BF16, D, G, G, 1, NW, 1>(a, w.b, w.gg, w.part, w.nparts, w.poisoned,
+                                             s_acc, s_m, s_l);
 }
 
 template <int D, int BS, int G>

@@ -73,8 +73,8 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
   __shared__ float s_l[NW][GW];
   st.to_lds(s_acc[wave], s_m[wave], s_l[wave], lane);
   __syncthreads();
-  finish_partition<DT, D, G, GW, HS, NW>(a, w.b, w.gg, w.part, w.nparts, w.poisoned, s_acc,
-                                             s_m, s_l);
+  finish_partition<DT, D, G, GW, HS, NW, NW / HS>(a, w.b, w.gg, w.part, w.nparts,
+                                                  w.poisoned, s_acc, s_m, s_l);
 }
 
 template <class DT, int D, int G, int NT>
