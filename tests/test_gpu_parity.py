@@ -207,6 +207,25 @@ def test_merge_paths_match_oracle(name, ps, merge, monkeypatch):
     G.assert_close(out, ref, w.dtype, f"{name} ps={ps} merge={merge}")
 
 
+@pytest.mark.parametrize("merge", ["inkernel", "separate"])
+@pytest.mark.parametrize("hpw", [1, 2, 4])
+@pytest.mark.parametrize("name,ps", [("f32_d128_bs32_g4", 64), ("bf16_d128_bs32_g2", 64),
+                                     ("bf16_d64_bs16_g2", 256)])
+def test_heads_per_workgroup_match_oracle(name, ps, hpw, merge, monkeypatch):
+    """Workgroups forced to take 1, 2 or 4 kv heads; split sequences merged by
+    the last partition to arrive (every kv head of its group in one pass, a
+    separate code path for each group size) or by the merge kernel."""
+    monkeypatch.setenv("PAGEDATTN_HEADS_PER_WG", str(hpw))
+    monkeypatch.setenv("PAGEDATTN_MERGE", merge)
+    inp = inputs_for(name)
+    w = inp["workload"]
+    say("write+decode", name, "partition", ps, "heads per workgroup", hpw, "merge", merge)
+    d = G.upload(inp)
+    out = G.host_f64(gpu_step(d, ps))
+    ref, _ = oracle_step(inp)
+    G.assert_close(out, ref, w.dtype, f"{name} ps={ps} hpw={hpw} merge={merge}")
+
+
 @pytest.mark.parametrize("ps", [16, 64, 256, 1024, 1040, 2048])
 def test_partition_sizes_agree(ps):
     inp = inputs_for("qwen3_0p6b")
