@@ -96,11 +96,13 @@ def kernel_source_hash() -> str:
 
 def decode_kernel_name(w) -> str:
     """The decode kernel the library runs for this workload: the matrix-core
-    kernel for bfloat16 with 8, 16 or 32 query heads per kv head, the
-    vector-ALU kernel otherwise."""
+    kernel for bfloat16 with 4, 8, 16 or 32 query heads per kv head (4 only
+    over block tables of at most 4096 tokens), the vector-ALU kernel
+    otherwise."""
     g = w.num_q_heads // w.num_kv_heads
-    return "decode_mfma_kernel" if w.dtype == "bf16" and g in (8, 16, 32) \
-        else "decode_partition_kernel"
+    long_table = w.max_blocks_per_seq * w.block_size > 4096
+    mfma = w.dtype == "bf16" and (g in (8, 16, 32) or (g == 4 and not long_table))
+    return "decode_mfma_kernel" if mfma else "decode_partition_kernel"
 
 
 def gather_then_attention(q, k_cache, v_cache, block_tables, context_lens, scale):

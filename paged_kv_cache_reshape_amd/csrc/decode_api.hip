@@ -4,7 +4,7 @@
 // The decode runs as fixed partitions: one workgroup per (kv-head group,
 // sequence, partition of partition_size tokens).  Two kernels share that
 // schedule, its workspace and its results: the matrix-core one
-// (decode_mfma.hip) for bfloat16 with 8, 16 or 32 query heads per kv head,
+// (decode_mfma.hip) for bfloat16 with 4, 8, 16 or 32 query heads per kv head,
 // the vector-ALU one (decode_partition.hip) for everything else.  When the
 // caller leaves the partition size to the library it picks, by shape, the
 // partition length and the kv heads per workgroup that measured fastest on
@@ -52,10 +52,19 @@ int auto_partition_tokens(int D, int max_tokens) {
   return max_tokens > 4096 ? 2048 : 1024;
 }
 
-// The matrix-core kernel where it applies.  PAGEDATTN_DECODE_KERNEL=valu
-// forces the vector-ALU kernel (tests compare the two).
-bool use_mfma(int dtype, int D, int bs, int G) {
+// The matrix-core kernel where it applies, except for groups of 4 over block
+// tables of more than 4096 tokens.  There every compute unit streams whole
+// partitions for the whole launch, and the vector kernel's two kv heads per
+// workgroup move more bytes per compute unit.  Measured on MI355X, the
+// 32K-token batch (G = 4) took 167 / 174 / 189 us on the vector kernel
+// against 177 / 181 / 194 us on the matrix cores at 2048 / 1024 / 512-token
+// partitions.  Over shorter, ragged tables the matrix cores win by 7-13% at
+// G = 4 (Llama-3.2-shaped batch 61.7 against 66.1 us).
+// PAGEDATTN_DECODE_KERNEL=valu forces the vector-ALU kernel (tests compare
+// the two).
+bool use_mfma(int dtype, int D, int bs, int G, int64_t span_tokens) {
   if (!mfma_supported(dtype, D, bs, G)) return false;
+  if (G == 4 && span_tokens > 4096) return false;
   const char* env = getenv("PAGEDATTN_DECODE_KERNEL");
   return !(env && strcmp(env, "valu") == 0);
 }
@@ -236,7 +245,8 @@ pa_status decode_impl(void* out, const void* q, bool step, const void* key, cons
   a.max_blocks = max_blocks_per_seq;
   a.part_blocks = plan.part_blocks;
   a.max_parts = plan.max_parts;
-  const bool mfma = use_mfma(dtype, head_dim, block_size, G);
+  const bool mfma = use_mfma(dtype, head_dim, block_size, G,
+                              (int64_t)max_blocks_per_seq * block_size);
   // The matrix-core kernel serves one kv head per workgroup (its eight waves
   // split the blocks).
   a.heads_per_wg = mfma ? 1 : plan.hpw;

@@ -37,7 +37,7 @@ hipError_t dispatch_decode(int dtype, int D, int BS, int G, F&& f) {
 hipError_t launch_partition(int dtype, int D, int BS, int G, const DecodeArgs& a,
                             hipStream_t s);
 
-// Matrix-core kernel for large query groups (bfloat16, G in {8, 16, 32}):
+// Matrix-core kernel for query groups of 4 or more (bfloat16, G in {4, 8, 16, 32}):
 // same arguments, workspace and results as launch_partition.
 bool mfma_supported(int dtype, int D, int BS, int G);
 hipError_t launch_mfma(int D, int BS, int G, const DecodeArgs& a, hipStream_t s);

@@ -1,11 +1,18 @@
-// Decode attention, fixed-size partitions, bfloat16 with large query groups
-// (G = 8, 16 or 32 query heads per kv head, MQA included): q.k and p.v both
+// Decode attention, fixed-size partitions, bfloat16 with query groups of
+// G = 4, 8, 16 or 32 query heads per kv head (MQA included): q.k and p.v both
 // run on the matrix cores (mfma_attn.hpp).
 //
 // Why a second kernel: with G query heads per kv head every K and V byte is
-// used G times, so at G >= 8 the vector-ALU kernel is bound by its multiply-
-// adds, not by HBM (G flops per byte against a vector ridge near 20).  On the
-// matrix cores the same work is a few instructions per 16-token tile.
+// used G times, and the vector-ALU kernel's multiply-adds, dot-product
+// reductions and conversions per byte grow with G until they, not HBM, set
+// its time.  On the matrix cores the same work is a few instructions per
+// 16-token tile; a 16-row tile with fewer than 16 live rows masks the rest.
+// Measured on MI355X: the MQA batch ran 527 GB/s on the vector kernel; at
+// G = 4 the Llama-3.2-shaped batch takes 61.5 against 66.3 us, and a
+// head_dim-128 batch of 32 sequences 35.5 against 39.8 us (the launcher keeps
+// G = 4 on the vector kernel for tables of more than 4096 tokens); at G = 2
+// the Qwen3-shaped batch is faster on the vector kernel (32.8 against 33.1 us
+// at best).
 //
 // Same partitioning, merge and workspace as the vector-ALU kernel: one
 // workgroup per kv-head group, sequence and partition; the last workgroup of
@@ -138,12 +145,13 @@ hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t stream) {
 
 bool mfma_supported(int dtype, int D, int BS, int G) {
   return dtype == PA_DTYPE_BF16 && (D == 64 || D == 128) && (BS == 16 || BS == 32) &&
-         (G == 8 || G == 16 || G == 32);
+         (G == 4 || G == 8 || G == 16 || G == 32);
 }
 
 hipError_t launch_mfma(int D, int BS, int G, const DecodeArgs& a, hipStream_t s) {
   auto by_g = [&](auto d, auto bs) -> hipError_t {
     switch (G) {
+      case 4: return launch_mfma_t<decltype(d)::value, decltype(bs)::value, 4>(a, s);
       case 8: return launch_mfma_t<decltype(d)::value, decltype(bs)::value, 8>(a, s);
       case 16: return launch_mfma_t<decltype(d)::value, decltype(bs)::value, 16>(a, s);
       case 32: return launch_mfma_t<decltype(d)::value, decltype(bs)::value, 32>(a, s);

@@ -149,7 +149,8 @@ def test_decode_matches_oracle(name):
     G.assert_close(out, ref, w.dtype, name)
 
 
-@pytest.mark.parametrize("name", ["mqa_large", "bf16_d64_bs32_g8", "bf16_d128_bs16_g16"])
+@pytest.mark.parametrize("name", ["mqa_large", "bf16_d64_bs32_g8", "bf16_d128_bs16_g16",
+                                  "llama32_1b", "bf16_d64_bs32_g4"])
 def test_vector_alu_kernel_matches_oracle(name, monkeypatch):
     """The vector-ALU kernel on shapes the matrix-core kernel takes by default."""
     monkeypatch.setenv("PAGEDATTN_DECODE_KERNEL", "valu")
