@@ -165,9 +165,10 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pair
  * The partition size (tokens) pa_paged_attention_decode will use for these
  * sizes: `requested` itself if it is a positive multiple of block_size no
  * larger than 128 * block_size; for `requested` 0 the library's own choice
- * (512 tokens at head_dim 64; at head_dim 128, 1024 tokens, or 2048 when
- * max_blocks_per_seq * block_size exceeds 4096 -- the fastest measured on
- * MI355X for the decode workloads); -1 if `requested` is invalid.
+ * (at head_dim 64, 512 tokens for 1 or 2 query heads per kv head and 1024
+ * for more; at head_dim 128, 1024 tokens, or 2048 when max_blocks_per_seq *
+ * block_size exceeds 4096 -- the fastest measured on MI355X for the decode
+ * workloads); -1 if `requested` is invalid.
  */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim,

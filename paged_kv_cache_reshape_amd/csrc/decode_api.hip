@@ -39,16 +39,18 @@ int heads_per_workgroup(int Hkv, int G, int D) {
   return 1;
 }
 
-// Library choice of partition length, from the head size and the longest
-// context the block table can describe.  Measured on MI355X over the decode
-// workloads (Qwen3-, Llama-3.2-shaped, long-context, large-batch MHA/MQA):
-// long partitions win -- a compute unit streams at most about 40 GB/s, so
-// what counts is that the longest partitions are few and large ones carry no
-// merge -- except at head_dim 64, where 512 tokens is better; tables of more
-// than 4096 tokens (the 32K-token batch: 191 us at 2048, 200 us at 1024)
-// take 2048.
-int auto_partition_tokens(int D, int max_tokens) {
-  if (D != 128) return 512;
+// Library choice of partition length, from the head size, the query group
+// and the longest context the block table can describe.  Measured on MI355X
+// over the decode workloads (Qwen3-, Llama-3.2-shaped, long-context,
+// large-batch MHA/MQA): long partitions win -- a compute unit streams at most
+// about 40 GB/s, so what counts is that the longest partitions are few and
+// large ones carry no merge -- with tables of more than 4096 tokens taking
+// 2048 (the 32K-token batch: 191 us at 2048, 200 us at 1024).  At head_dim 64
+// the vector kernel (G <= 2) does better with 512 tokens; groups of 4 or
+// more, on the matrix cores for bfloat16, take 1024 (Llama-3.2-shaped batch
+// 61.0 against 61.3 us, 32-token blocks 66.4 against 73.3 us).
+int auto_partition_tokens(int D, int G, int max_tokens) {
+  if (D != 128) return G >= 4 ? 1024 : 512;
   return max_tokens > 4096 ? 2048 : 1024;
 }
 
@@ -93,7 +95,7 @@ bool make_plan(int B, int Hq, int Hkv, int D, int max_blocks, int bs, int reques
   const int G = Hq / Hkv;
   if (!group_supported(G)) return false;
   p->hpw = heads_per_workgroup(Hkv, G, D);
-  const int tokens = requested == 0 ? auto_partition_tokens(D, max_blocks * bs) : requested;
+  const int tokens = requested == 0 ? auto_partition_tokens(D, G, max_blocks * bs) : requested;
   if (tokens < 0 || tokens % bs != 0) return false;
   const int pb = tokens / bs;
   if (pb < 1 || pb > kMaxPartitionBlocks) return false;

@@ -172,13 +172,15 @@ def test_partition_size_rule(lib):
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 64) == 1024
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 128) == 2048
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 129) == -1
-    # left to the library: 1024 tokens at head_dim 128, 512 at head_dim 64
+    # left to the library: 1024 tokens at head_dim 128; at head_dim 64, 512
+    # for groups of 1 or 2 query heads, 1024 for more
     assert pa.decode_partition_size(32, 16, 8, 128, 128, 16, 0) == 1024
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 0) == 2048
     assert pa.decode_partition_size(8, 32, 8, 128, 256, 16, 0) == 1024
     assert pa.decode_partition_size(8, 32, 8, 128, 257, 16, 0) == 2048
     assert pa.decode_partition_size(256, 32, 32, 128, 32, 32, 0) == 1024
-    assert pa.decode_partition_size(64, 32, 8, 64, 256, 16, 0) == 512
+    assert pa.decode_partition_size(64, 32, 8, 64, 256, 16, 0) == 1024
+    assert pa.decode_partition_size(64, 16, 8, 64, 256, 16, 0) == 512
     assert pa.decode_partition_size(4, 4, 2, 64, 4, 16, 0) == 512
 
 
