@@ -550,29 +550,10 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
     }
     __syncthreads();
   }
-  for (int e = tid; e < wg_elems; e += NT) {
-    const int hwe = e / (G * D), rem = e % (G * D);
-    const int hh = rem / D, d = rem % D;
-    const int r = e / D;
-    const int w0 = hwe + hpw * (hh / GW);
-    const int h = hh % GW;
-    float M, L, A = 0.0f;
-    if constexpr (kRowFactors) {
-      for (int t = 0; t < nwt; ++t) A += s_acc[w0 + hpw * HS * t][h][d] * s_fac[t * rows + r];
-      M = s_rm[r];
-      L = s_rl[r];
-    } else {
-      M = kNoMax;
-      for (int t = 0; t < nwt; ++t) M = fmaxf(M, s_m[w0 + hpw * HS * t][h]);
-      L = 0.0f;
-      for (int t = 0; t < nwt; ++t) {
-        const int w = w0 + hpw * HS * t;
-        const float f = fast_exp2(s_m[w][h] - M);
-        L += s_l[w][h] * f;
-        A += s_acc[w][h][d] * f;
-      }
-      if (poisoned) L = __builtin_nanf("");
-    }
+  // Output element e (row r = e / D of the group, kv head hwe, query head hh,
+  // dimension d) with combined sum A, row maximum M and row sum L: the
+  // normalised output, or the partition's state for the merge.
+  const auto emit = [&](int e, int hwe, int hh, int d, float A, float M, float L) {
     if (nparts == 1) {
       store_out(DT{}, a.out, out_base + e, A / L);
     } else {
@@ -591,6 +572,49 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
           publish(a.ws_ml + pr * 2 + 1, L);
         }
       }
+    }
+  };
+  if constexpr (kRowFactors) {
+    // Four consecutive elements of one row per thread: one 16-byte LDS read
+    // per wave share (each element sums its shares in the same order).
+    static_assert(D % 4 == 0, "rows split into 4-element pieces");
+    for (int e = 4 * tid; e < wg_elems; e += 4 * NT) {
+      const int hwe = e / (G * D), rem = e % (G * D);
+      const int hh = rem / D, d = rem % D;
+      const int r = e / D;
+      const int w0 = hwe + hpw * (hh / GW);
+      const int h = hh % GW;
+      float A0 = 0.0f, A1 = 0.0f, A2 = 0.0f, A3 = 0.0f;
+      for (int t = 0; t < nwt; ++t) {
+        const float4 v = *reinterpret_cast<const float4*>(&s_acc[w0 + hpw * HS * t][h][d]);
+        const float f = s_fac[t * rows + r];
+        A0 += v.x * f;
+        A1 += v.y * f;
+        A2 += v.z * f;
+        A3 += v.w * f;
+      }
+      const float M = s_rm[r], L = s_rl[r];
+      emit(e, hwe, hh, d, A0, M, L);
+      emit(e + 1, hwe, hh, d + 1, A1, M, L);
+      emit(e + 2, hwe, hh, d + 2, A2, M, L);
+      emit(e + 3, hwe, hh, d + 3, A3, M, L);
+    }
+  } else {
+    for (int e = tid; e < wg_elems; e += NT) {
+      const int hwe = e / (G * D), rem = e % (G * D);
+      const int hh = rem / D, d = rem % D;
+      const int w0 = hwe + hpw * (hh / GW);
+      const int h = hh % GW;
+      float M = kNoMax, L = 0.0f, A = 0.0f;
+      for (int t = 0; t < nwt; ++t) M = fmaxf(M, s_m[w0 + hpw * HS * t][h]);
+      for (int t = 0; t < nwt; ++t) {
+        const int w = w0 + hpw * HS * t;
+        const float f = fast_exp2(s_m[w][h] - M);
+        L += s_l[w][h] * f;
+        A += s_acc[w][h][d] * f;
+      }
+      if (poisoned) L = __builtin_nanf("");
+      emit(e, hwe, hh, d, A, M, L);
     }
   }
   if (nparts == 1 || a.deferred_merge) return;

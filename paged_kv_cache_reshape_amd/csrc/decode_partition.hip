@@ -68,7 +68,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
   stream_blocks<NI>(tw, nwt, w.nblk_run, fetch, consume);
   st.merge_rows();
 
-  __shared__ float s_acc[NW][GW][D];
+  __shared__ __attribute__((aligned(16))) float s_acc[NW][GW][D];
   __shared__ float s_m[NW][GW];
   __shared__ float s_l[NW][GW];
   st.to_lds(s_acc[wave], s_m[wave], s_l[wave], lane);
