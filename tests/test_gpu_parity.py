@@ -36,6 +36,8 @@ EXTRA = {
                                         ("uniform", 1, 700), num_blocks=120, seed=36),
     "bf16_d64_bs32_g4": synth.Workload("bf16_d64_bs32_g4", 6, 16, 4, 64, 32, "bf16",
                                        ("uniform", 1, 900), num_blocks=200, seed=37),
+    "bf16_d128_bs16_g4": synth.Workload("bf16_d128_bs16_g4", 6, 16, 4, 128, 16, "bf16",
+                                        ("uniform", 1, 1500), seed=38),
 }
 
 
@@ -150,7 +152,7 @@ def test_decode_matches_oracle(name):
 
 
 @pytest.mark.parametrize("name", ["mqa_large", "bf16_d64_bs32_g8", "bf16_d128_bs16_g16",
-                                  "llama32_1b", "bf16_d64_bs32_g4"])
+                                  "llama32_1b", "bf16_d64_bs32_g4", "bf16_d128_bs16_g4"])
 def test_vector_alu_kernel_matches_oracle(name, monkeypatch):
     """The vector-ALU kernel on shapes the matrix-core kernel takes by default."""
     monkeypatch.setenv("PAGEDATTN_DECODE_KERNEL", "valu")
