@@ -229,6 +229,23 @@ def test_heads_per_workgroup_match_oracle(name, ps, hpw, merge, monkeypatch):
     G.assert_close(out, ref, w.dtype, f"{name} ps={ps} hpw={hpw} merge={merge}")
 
 
+@pytest.mark.parametrize("G_", [4, 8, 16, 32])
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("D", [64, 128])
+def test_matrix_core_kernel_every_shape(D, bs, G_):
+    """Every (head_dim, block size, group) the matrix-core kernel is built
+    for, on a small ragged batch that splits its longer sequences."""
+    hkv = 2 if G_ <= 16 else 1
+    w = synth.Workload(f"mfma_d{D}_bs{bs}_g{G_}", 4, G_ * hkv, hkv, D, bs, "bf16",
+                       ("uniform", 1, 600), seed=40 + D + bs + G_)
+    inp = synth.make_inputs(w)
+    say("write+decode", w.name, "partition 128")
+    d = G.upload(inp)
+    out = G.host_f64(gpu_step(d, 128))
+    ref, _ = oracle_step(inp)
+    G.assert_close(out, ref, "bf16", w.name)
+
+
 @pytest.mark.parametrize("ps", [16, 64, 256, 1024, 1040, 2048])
 def test_partition_sizes_agree(ps):
     inp = inputs_for("qwen3_0p6b")
