@@ -246,6 +246,26 @@ def test_matrix_core_kernel_every_shape(D, bs, G_):
     G.assert_close(out, ref, "bf16", w.name)
 
 
+@pytest.mark.parametrize("G_", [1, 2, 4, 8, 16, 32])
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_vector_kernel_every_shape(dtype, D, bs, G_, monkeypatch):
+    """Every (dtype, head_dim, block size, group) the vector-ALU kernel is
+    built for (forced where the matrix cores would take the shape), on a
+    small ragged batch that splits its longer sequences."""
+    monkeypatch.setenv("PAGEDATTN_DECODE_KERNEL", "valu")
+    hkv = 2 if G_ <= 16 else 1
+    w = synth.Workload(f"valu_{dtype}_d{D}_bs{bs}_g{G_}", 4, G_ * hkv, hkv, D, bs, dtype,
+                       ("uniform", 1, 600), seed=60 + D + bs + G_)
+    inp = synth.make_inputs(w)
+    say("write+decode (vector ALU kernel)", w.name, "partition 128")
+    d = G.upload(inp)
+    out = G.host_f64(gpu_step(d, 128))
+    ref, _ = oracle_step(inp)
+    G.assert_close(out, ref, dtype, w.name)
+
+
 @pytest.mark.parametrize("ps", [16, 64, 256, 1024, 1040, 2048])
 def test_partition_sizes_agree(ps):
     inp = inputs_for("qwen3_0p6b")
