@@ -718,6 +718,24 @@ def test_prefill_matches_oracle(name, ks, monkeypatch):
 
 
 @pytest.mark.parametrize("ks", ["1", "2"])
+@pytest.mark.parametrize("G_", [1, 2, 4, 8, 16, 32])
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_every_shape(D, bs, G_, ks, monkeypatch):
+    """Every (head_dim, block size, group) the prefill kernel is built for,
+    in both forms, on chunks after cached prefixes (small ragged batch)."""
+    monkeypatch.setenv("PAGEDATTN_PREFILL_KSPLIT", ks)
+    hkv = 2 if G_ <= 16 else 1
+    w = synth.Workload(f"pf_d{D}_bs{bs}_g{G_}", 2, G_ * hkv, hkv, D, bs, "bf16",
+                       ("uniform", 40, 300), seed=80 + D + bs + G_, query=("uniform", 1, 200))
+    inp = synth.make_prefill_inputs(w)
+    say("prefill", w.name, "key halves", ks)
+    d, out = prefill_gpu(inp)
+    ref, _ = prefill_oracle(inp)
+    G.assert_close(G.host_f64(out), ref, "bf16", w.name)
+
+
+@pytest.mark.parametrize("ks", ["1", "2"])
 def test_prefill_ragged_with_empty_and_bad_sequences(ks, monkeypatch):
     """A sequence with no new tokens writes nothing; a sequence claiming more
     new tokens than positions gets NaN rows; the others are unaffected."""
