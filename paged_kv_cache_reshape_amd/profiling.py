@@ -84,6 +84,12 @@ def traffic_record(fetch_csv: str, write_csv: str, workload: str, partition_size
     copy_key = max((k for k in fetch if k.startswith("copy")), key=lambda k: fetch[k])
     fetch_factor = k_cache_bytes / 1024.0 / fetch[copy_key]
     write_factor = k_cache_bytes / 1024.0 / write[copy_key]
+    # WRITE_SIZE reads a clone's bytes exactly; far from that, the run made no
+    # clone (a pool too large to replicate keeps one copy) and the counters
+    # have nothing of known size to be scaled by.
+    if not 0.9 <= write_factor <= 1.1:
+        raise ValueError(f"the largest copy kernel wrote {write[copy_key]:.1f} KiB, not one "
+                         f"K cache ({k_cache_bytes / 1024.0:.1f} KiB): no clone to scale by")
     read_b = fetch["decode"] * fetch_factor * 1024.0
     write_b = write["decode"] * write_factor * 1024.0
     # Counters of a `bench.py --step-only` run see only the fused step's

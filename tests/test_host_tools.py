@@ -75,6 +75,21 @@ def test_traffic_record_is_scaled_by_the_copy_kernel(tmp_path, monkeypatch, fuse
     assert bench.traffic_record(wl) is None
 
 
+def test_traffic_record_needs_a_clone_of_known_size(tmp_path, monkeypatch):
+    """Without a copy kernel that cloned one K pool (a run that kept a single
+    pool copy), the counters cannot be scaled and no record is written."""
+    wl = "tiny_f32"
+    dec = "void pa::decode_partition_kernel<pa::F32, 64, 16, 2, 4>(pa::DecodeArgs)"
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    _counter_csv(fetch, "FETCH_SIZE", [("__amd_rocclr_copyBuffer", 1.0, 3), (dec, 100.0, 64)])
+    _counter_csv(write, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 1.0, 3), (dec, 2.0, 64)])
+    monkeypatch.setattr(bench, "traffic_file",
+                        lambda workload: str(tmp_path / f"traffic_{workload}.json"))
+    with pytest.raises(ValueError, match="no clone"):
+        profiling.traffic_record(str(fetch), str(write), wl, 512, "the commands", True)
+    assert not os.path.exists(tmp_path / f"traffic_{wl}.json")
+
+
 def test_bench_refuses_more_than_one_gpu():
     """One GPU only: with --gpus 2 the benchmark says so and exits with 2."""
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
