@@ -71,6 +71,14 @@ const char* pa_status_string(int32_t status);
 const char* pa_last_error_message(void);
 
 /*
+ * Re-read the PAGEDATTN_* environment overrides of the library's own choices
+ * (schedule, kernel, merge path, workers; for tests and tuning runs).  They
+ * are read once, at the first call that needs them, and again only here; a
+ * call running on another thread meanwhile uses one whole set, old or new.
+ */
+void pa_reload_options(void);
+
+/*
  * Paged KV write (the cache's logical-to-physical write; barellm README,
  * paged-cache component list).
  *

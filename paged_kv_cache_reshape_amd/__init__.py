@@ -16,6 +16,7 @@ Functions (names follow the C ABI in ``include/pagedattn.h``):
   copy_blocks(k_cache, v_cache, block_pairs)
   decode_partition_size(...), decode_workspace_bytes(...)
   debug_gather_kv(k_cache, v_cache, block_tables, context_lens)
+  reload_options()   re-read the PAGEDATTN_* overrides (tests, tuning)
 """
 from __future__ import annotations
 
@@ -31,7 +32,7 @@ __all__ = [
     "LIB_PATH", "load_library", "PagedAttnError", "reshape_and_cache",
     "paged_attention_decode", "decode_step", "paged_attention_prefill", "copy_blocks",
     "decode_partition_size", "decode_workspace_bytes", "debug_gather_kv", "workspace_for",
-    "counters_for",
+    "counters_for", "reload_options",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
@@ -72,6 +73,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.pa_status_string.argtypes = [i32]
         lib.pa_last_error_message.restype = ctypes.c_char_p
         lib.pa_last_error_message.argtypes = []
+        lib.pa_reload_options.restype = None
+        lib.pa_reload_options.argtypes = []
         lib.pa_reshape_and_cache.restype = i32
         lib.pa_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                              i32, i32, vp]
@@ -98,6 +101,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                            i32, i32, i32, vp]
         _lib = lib
         return lib
+
+
+def reload_options() -> None:
+    """Make the library re-read its PAGEDATTN_* environment overrides (it
+    reads them once otherwise); the workspace sizes cached here follow."""
+    load_library().pa_reload_options()
+    decode_workspace_bytes.cache_clear()
 
 
 def _check(status: int, what: str) -> None:

@@ -25,8 +25,8 @@ LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 ARCH = "gfx950"
-HIP_SOURCES = ["decode_api.hip", "decode_partition.hip", "decode_mfma.hip", "prefill_mfma.hip",
-               "kv_write.hip"]
+HIP_SOURCES = ["decode_api.hip", "decode_partition.hip", "decode_mfma.hip", "decode_stream.hip",
+               "prefill_mfma.hip", "kv_write.hip"]
 HOST_SOURCES = ["status.cpp"]
 
 HIPCC_FLAGS = [
@@ -81,7 +81,7 @@ def build(verbose: bool = False, jobs: int = 4, defines=(), out: str | None = No
     for src in HOST_SOURCES:
         obj = os.path.join(build_dir, src + ".o")
         objs.append(obj)
-        cmds.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}",
+        cmds.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}",
                      "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))

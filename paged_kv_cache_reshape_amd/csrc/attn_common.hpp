@@ -36,6 +36,7 @@ struct DecodeArgs {
   int32_t max_parts;     // partition kernel: partitions per sequence, at most
   int32_t heads_per_wg;  // consecutive kv heads one workgroup takes (1, 2 or 4)
   int32_t deferred_merge;  // 1: partitions store their states and a second kernel merges
+  int32_t stream_workers;  // stream schedule: worker waves per kv head (0: fixed partitions)
   float scale_log2;      // scale * log2(e): scores are kept in base-2 units
   // Decode step with the KV write fused in: this step's token of sequence b
   // ([num_seqs, num_kv_heads, D] rows), written at position ctx - 1 before
@@ -113,6 +114,51 @@ __device__ __forceinline__ float collect(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_SYSTEM);
 }
+
+// The same system-coherent policy (sc0 sc1, what a system-scope atomic
+// store or load carries on gfx950) for whole 16- or 8-byte pieces, through a
+// buffer resource over a wave-uniform base: partial states move in a few
+// wide accesses instead of one 4-byte transaction per value.
+constexpr int kBufferWord3 = 0x00020000;  // gfx9 raw buffer, 32-bit data format
+constexpr int kSystemCoherent = 17;       // cache-policy operand: sc0 | sc1
+struct CoherentRegion {
+  __amdgpu_buffer_rsrc_t r;
+  // base must be the same in every lane; accesses are range-checked against
+  // `bytes` (an access past it reads 0 and writes nothing).
+  __device__ __forceinline__ CoherentRegion(float* base, uint32_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, kBufferWord3)) {}
+  __device__ __forceinline__ void store4(uint32_t off, float a, float b, float c, float d) const {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    const u4 v = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kSystemCoherent);
+  }
+  __device__ __forceinline__ void store2(uint32_t off, float a, float b) const {
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    const u2 v = {__float_as_uint(a), __float_as_uint(b)};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kSystemCoherent);
+  }
+  __device__ __forceinline__ void store1(uint32_t off, float a) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), r, off, 0, kSystemCoherent);
+  }
+  // N consecutive floats (N in {1, 2, 4, 8, 16}) at byte offset off.
+  template <int N>
+  __device__ __forceinline__ void load(uint32_t off, float* x) const {
+    if constexpr (N == 1) {
+      x[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSystemCoherent));
+    } else if constexpr (N == 2) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kSystemCoherent);
+      x[0] = __uint_as_float(v[0]);
+      x[1] = __uint_as_float(v[1]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < N / 4; ++k) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * k, 0, kSystemCoherent);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[4 * k + t] = __uint_as_float(v[t]);
+      }
+    }
+  }
+};
 
 // Running-state sentinel: finite, so exp2(sentinel - sentinel) = 1 for rows
 // that have seen no token yet (their sum and output are still zero).

@@ -1,18 +1,24 @@
 // C ABI of the decode: argument checks, the choice of kernel and schedule,
 // workspace layout and the launch.
 //
-// The decode runs as fixed partitions: one workgroup per (kv-head group,
-// sequence, partition of partition_size tokens).  Two kernels share that
-// schedule, its workspace and its results: the matrix-core one
-// (decode_mfma.hip) for bfloat16 with 4, 8, 16 or 32 query heads per kv head,
-// the vector-ALU one (decode_partition.hip) for everything else.  When the
-// caller leaves the partition size to the library it picks, by shape, the
-// partition length and the kv heads per workgroup that measured fastest on
-// MI355X for the decode workloads (see auto_partition_tokens).
+// Two schedules.  The balanced ("stream") one (decode_stream.hip) cuts each
+// kv head's list of the batch's blocks into equal ranges, one per worker
+// wave, so that every compute unit streams the same bytes whatever the
+// context lengths; it serves the library's choice for batches of few
+// (sequence, kv head) pairs with 1 or 2 query heads per kv head.  The fixed
+// one gives each (kv-head group, sequence, partition of partition_size
+// tokens) a workgroup; two kernels share it, its workspace and its results:
+// the matrix-core one (decode_mfma.hip) for bfloat16 with 4, 8, 16 or 32
+// query heads per kv head, the vector-ALU one (decode_partition.hip) for the
+// rest.  A caller that fixes partition_size gets the fixed schedule with
+// that size (the long-context workload states 512-token partitions).
 #include "decode_launch.hpp"
+#include "options.hpp"
+#include "stream_sched.hpp"
 
-#include <stdlib.h>
 #include <string.h>
+
+#include <algorithm>
 
 namespace pa {
 namespace {
@@ -31,10 +37,8 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // overrides the choice (1, 2 or 4) for experiments.
 int heads_per_workgroup(int Hkv, int G, int D) {
   const int hs = G > 8 ? G / 8 : 1;
-  if (const char* env = getenv("PAGEDATTN_HEADS_PER_WG")) {
-    const int v = atoi(env);
-    if ((v == 1 || v == 2 || v == 4) && Hkv % v == 0 && v * hs <= kDecodeWaves) return v;
-  }
+  const int v = options().heads_per_wg;
+  if ((v == 1 || v == 2 || v == 4) && Hkv % v == 0 && v * hs <= kDecodeWaves) return v;
   if (D == 128 && Hkv % 2 == 0 && 2 * hs <= kDecodeWaves) return 2;
   return 1;
 }
@@ -67,27 +71,49 @@ int auto_partition_tokens(int D, int G, int max_tokens) {
 bool use_mfma(int dtype, int D, int bs, int G, int64_t span_tokens) {
   if (!mfma_supported(dtype, D, bs, G)) return false;
   if (G == 4 && span_tokens > 4096) return false;
-  const char* env = getenv("PAGEDATTN_DECODE_KERNEL");
-  return !(env && strcmp(env, "valu") == 0);
+  return !options().valu_only;
 }
 
 // PAGEDATTN_MERGE=separate / inkernel forces where split sequences are
 // merged (the tests run both paths).
 bool deferred_merge(int max_parts) {
-  const char* env = getenv("PAGEDATTN_MERGE");
-  if (env && strcmp(env, "separate") == 0) return true;
-  if (env && strcmp(env, "inkernel") == 0) return false;
+  if (options().merge == 1) return true;
+  if (options().merge == 2) return false;
   return max_parts >= 16;
 }
 
+// Where the stream schedule merges split sequences: in the launch, by the
+// last worker to finish (default), or in a merge kernel launched after it
+// (PAGEDATTN_MERGE=separate; PAGEDATTN_MERGE=inkernel forces the default).
+bool stream_deferred_merge() { return options().merge == 1; }
+
+// Worker waves in all that the stream schedule aims for: one workgroup of
+// kStreamWaves on each of the 256 compute units.
+constexpr int kStreamWorkersAll = 1024;
+
+// The stream schedule where it is the library's choice: 1 or 2 query heads
+// per kv head (larger groups keep the matrix-core kernel), and few enough
+// (sequence, kv head) pairs that the fixed schedule would leave compute units
+// without work or unevenly loaded.  PAGEDATTN_SCHEDULE=fixed|stream forces
+// either (stream only where it is built).
+bool stream_eligible(int B, int Hkv, int G, int max_blocks, int requested) {
+  if (requested != 0 || !stream_supported(G)) return false;
+  if (B > kStreamMaxSeqs || max_blocks > 0xFFFF) return false;
+  if (options().schedule == 1) return false;
+  if (options().schedule == 2) return true;
+  return G <= 2 && (int64_t)B * Hkv <= kStreamWorkersAll;
+}
+
 struct Plan {
+  bool stream;
+  int stream_workers;  // per kv head
   int part_blocks;
   int max_parts;
   int hpw;
   size_t acc_bytes, ml_bytes, total;
 };
 
-// The partitioning and workspace for these sizes; false if invalid.
+// The schedule and workspace for these sizes; false if invalid.
 bool make_plan(int B, int Hq, int Hkv, int D, int max_blocks, int bs, int requested,
                Plan* p) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || max_blocks <= 0) return false;
@@ -102,7 +128,29 @@ bool make_plan(int B, int Hq, int Hkv, int D, int max_blocks, int bs, int reques
   p->part_blocks = pb;
   p->max_parts = (max_blocks + pb - 1) / pb;
   p->acc_bytes = p->ml_bytes = p->total = 0;
-  if (p->max_parts <= 1 || B == 0) return true;
+  p->stream = false;
+  p->stream_workers = 0;
+  if (B == 0) return true;
+  if (stream_eligible(B, Hkv, G, max_blocks, requested)) {
+    // Workers per kv head: the aim, and enough that no range exceeds
+    // kStreamMaxRange blocks however the lengths fall; a multiple of the
+    // waves of a workgroup.
+    const int64_t all = options().stream_workers > 0 ? options().stream_workers
+                                                      : kStreamWorkersAll;
+    int64_t R = (all + Hkv - 1) / Hkv;
+    R = std::max<int64_t>(R, ((int64_t)B * max_blocks + kStreamMaxRange - 1) / kStreamMaxRange);
+    R = (R + kStreamWaves - 1) / kStreamWaves * kStreamWaves;
+    if (R * Hkv <= (int64_t)1 << 22) {
+      p->stream = true;
+      p->stream_workers = (int)R;
+      const size_t rows = (size_t)Hkv * R * 2 * G;
+      p->acc_bytes = align256(rows * D * sizeof(float));
+      p->ml_bytes = align256(rows * 2 * sizeof(float));
+      p->total = p->acc_bytes + p->ml_bytes;
+      return true;
+    }
+  }
+  if (p->max_parts <= 1) return true;
   const size_t rows = (size_t)B * Hkv * p->max_parts * G;
   p->acc_bytes = align256(rows * D * sizeof(float));
   p->ml_bytes = align256(rows * 2 * sizeof(float));
@@ -123,7 +171,7 @@ extern "C" int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_head
   if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
                  block_size, requested, &p))
     return -1;
-  return p.part_blocks * block_size;
+  return p.stream ? 0 : p.part_blocks * block_size;
 }
 
 extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
@@ -195,7 +243,7 @@ pa_status decode_impl(void* out, const void* q, bool step, const void* key, cons
               "between 1 and 128 blocks", partition_size, block_size);
     return PA_ERR_INVALID_ARGUMENT;
   }
-  if (plan.max_parts > 65535) {
+  if (!plan.stream && plan.max_parts > 65535) {
     set_error("%d partitions per sequence (max 65535): raise partition_size",
               plan.max_parts);
     return PA_ERR_UNSUPPORTED;
@@ -247,25 +295,30 @@ pa_status decode_impl(void* out, const void* q, bool step, const void* key, cons
   a.max_blocks = max_blocks_per_seq;
   a.part_blocks = plan.part_blocks;
   a.max_parts = plan.max_parts;
-  const bool mfma = use_mfma(dtype, head_dim, block_size, G,
-                              (int64_t)max_blocks_per_seq * block_size);
+  a.stream_workers = plan.stream_workers;
+  const bool mfma = !plan.stream && use_mfma(dtype, head_dim, block_size, G,
+                                             (int64_t)max_blocks_per_seq * block_size);
   // The matrix-core kernel serves one kv head per workgroup (its eight waves
   // split the blocks).
   a.heads_per_wg = mfma ? 1 : plan.hpw;
-  a.deferred_merge = plan.max_parts > 1 && deferred_merge(plan.max_parts);
+  a.deferred_merge = plan.stream ? stream_deferred_merge()
+                                 : plan.max_parts > 1 && deferred_merge(plan.max_parts);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.new_k = step ? key : nullptr;
   a.new_v = step ? value : nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t err = mfma ? launch_mfma(head_dim, block_size, G, a, s)
-                             : launch_partition(dtype, head_dim, block_size, G, a, s);
+  const hipError_t err = plan.stream ? launch_stream(dtype, head_dim, block_size, G, a, s)
+                         : mfma      ? launch_mfma(head_dim, block_size, G, a, s)
+                                     : launch_partition(dtype, head_dim, block_size, G, a, s);
   if (err != hipSuccess) {
     set_error("decode launch failed: %s", hipGetErrorString(err));
     return PA_ERR_HIP;
   }
   if (a.deferred_merge) {
-    const hipError_t merr = launch_merge(dtype, head_dim, block_size, G, a, s);
+    const hipError_t merr = plan.stream
+                                ? launch_stream_merge(dtype, head_dim, block_size, G, a, s)
+                                : launch_merge(dtype, head_dim, block_size, G, a, s);
     if (merr != hipSuccess) {
       set_error("merge launch failed: %s", hipGetErrorString(merr));
       return PA_ERR_HIP;

@@ -42,6 +42,22 @@ hipError_t launch_partition(int dtype, int D, int BS, int G, const DecodeArgs& a
 bool mfma_supported(int dtype, int D, int BS, int G);
 hipError_t launch_mfma(int D, int BS, int G, const DecodeArgs& a, hipStream_t s);
 
+constexpr int kStreamWaves = 4;  // worker waves per workgroup of the stream schedule
+
+// Kv heads one stream workgroup takes (one wave each, over kStreamWaves / HW
+// consecutive ranges): as many as divide both the waves and the kv heads.
+__host__ __device__ inline int stream_heads_per_wg(int Hkv) {
+  return Hkv % 4 == 0 ? 4 : Hkv % 2 == 0 ? 2 : 1;
+}
+
+// Balanced schedule (decode_stream.hip): worker waves over equal ranges of
+// each kv head's block list, G in {1, 2, 4}; same workspace contract.
+bool stream_supported(int G);
+hipError_t launch_stream(int dtype, int D, int BS, int G, const DecodeArgs& a, hipStream_t s);
+// Merge kernel run after a stream launch with deferred_merge set.
+hipError_t launch_stream_merge(int dtype, int D, int BS, int G, const DecodeArgs& a,
+                               hipStream_t s);
+
 // Merge kernel run after a partition launch with deferred_merge set.
 hipError_t launch_merge(int dtype, int D, int BS, int G, const DecodeArgs& a, hipStream_t s);
 

@@ -1,0 +1,345 @@
+// Decode attention on the balanced schedule (stream_sched.hpp), vector-ALU
+// worker: every wave is an independent worker over an equal range of one kv
+// head's block list, holding the G query heads of that kv head for one
+// sequence at a time (the per-row online softmax of RowAttn).  A workgroup
+// is kStreamWaves workers of the same kv head over consecutive ranges; after
+// the shared prefix sum there is no workgroup barrier, and no cross-wave
+// combine: a wave finishes each sequence it holds on its own.
+//
+// Per block the wave loads the K and V rows of its kv head (full-row 16-byte
+// loads, two blocks in flight), the query rows of the block's sequence (a
+// 512-byte read that hits the L2 after the sequence's first block) and, in a
+// decode step, the step's new K/V rows.  In a decode step the block holding
+// position ctx - 1 takes the new rows in place of what it read there, and the
+// wave writes them to the cache -- nothing else in the launch reads that row,
+// so the result is the write followed by the read, bit for bit.
+#include "stream_sched.hpp"
+
+#include "decode_launch.hpp"
+
+namespace pa {
+
+// 16-byte chunk of E output values: bf16 rounded to nearest even, or f32.
+__device__ __forceinline__ uint4 out_chunk(BF16, const float* x) {
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    w[k] = (uint32_t)f32_to_bf16_rne(x[2 * k]) | ((uint32_t)f32_to_bf16_rne(x[2 * k + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ __forceinline__ uint4 out_chunk(F32, const float* x) {
+  return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                    __float_as_uint(x[3]));
+}
+
+template <class DT, int D, int BS, int G, bool FUSED>
+__global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(DecodeArgs a) {
+  using Sh = DecodeShape<DT, D, BS, G, 1>;
+  using Row = RowAttn<DT, D, BS, G, 1>;
+  using S = typename DT::storage;
+  constexpr int E = Sh::E, RL = Sh::RL, ROWS = Sh::ROWS, NI = Sh::NI;
+  constexpr int NT = kStreamWaves * 64;
+  // Two blocks in flight; one where a block's rows already take 64 registers
+  // for K and V (float32 at head_dim 128 with 32-token blocks).
+  constexpr int PF = NI <= 8 ? 2 : 1;
+  static_assert(G <= 8, "one wave holds every query head of its kv head");
+
+  __shared__ int s_cum[kStreamMaxSeqs + 1];
+  __shared__ int s_part[kStreamWaves];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Hkv = a.num_kv_heads, Hq = a.num_q_heads;
+  // The workgroup's waves take HW neighbouring kv heads (one each) of RW
+  // consecutive ranges: their loads then cover HW * D * elt contiguous bytes
+  // of each token row, which measured far steadier per-wave rates than waves
+  // of one head over four ranges (MI355X, Qwen3-shaped batch: streaming
+  // times spread 19-29 us across waves with one head per workgroup).
+  const int HW = stream_heads_per_wg(Hkv);
+  const int RW = kStreamWaves / HW;
+  const int ngr = Hkv / HW;
+  const int gg = blockIdx.x % ngr, kwg = blockIdx.x / ngr;
+  const int h = gg * HW + wave % HW;
+  const int wgs_per_group = a.stream_workers / RW;
+
+  // Empty sequences give zero rows, lengths past the table NaN rows; each is
+  // written for this workgroup's kv heads by one workgroup of the group.
+  const int T = stream_prefix<NT>(a, BS, s_cum, s_part, [&](int b, int c) {
+    if (b % wgs_per_group != kwg) return;
+    const size_t base = ((size_t)b * Hq + (size_t)gg * HW * G) * D;
+    const float fill = c == 0 ? 0.0f : __builtin_nanf("");
+    for (int e = 0; e < HW * G * D; ++e) store_out(DT{}, a.out, base + e, fill);
+  });
+
+  // With fewer blocks than workers, the first T workers take one block each
+  // and the rest none: every worker in [0, R) then holds a block, which the
+  // piece count of a merge relies on.
+  const int R = min(a.stream_workers, T);
+  const int r = kwg * RW + wave / HW;
+  if (r >= R) return;
+  StreamRange w;
+  stream_range(a, s_cum, T, R, r, lane, w);
+
+  const int row = lane / RL, col = lane % RL;
+  const size_t tok_stride = (size_t)Hkv * D;
+  const size_t blk_stride = tok_stride * BS;
+  const size_t lane_off = (size_t)row * tok_stride + (size_t)h * D + col * E;
+  const S* kbase = static_cast<const S*>(a.k_cache) + lane_off;
+  const S* vbase = static_cast<const S*>(a.v_cache) + lane_off;
+  const S* qbase = static_cast<const S*>(a.q) + (size_t)h * G * D + col * E;
+  const S* nkbase = FUSED ? static_cast<const S*>(a.new_k) + (size_t)h * D + col * E : nullptr;
+  const S* nvbase = FUSED ? static_cast<const S*>(a.new_v) + (size_t)h * D + col * E : nullptr;
+
+  struct Slot {
+    uint4 k[NI], v[NI], q[G], nk, nv;
+  };
+  auto fetch = [&](int i, Slot& sl) {
+    const size_t off = (size_t)w.entry(i) * blk_stride;
+    const int b = (w.seqblk(i) >> 16) & 0x7FFF;
+    Row::fetch(kbase + off, vbase + off, tok_stride, sl.k, sl.v);
+#pragma unroll
+    for (int gh = 0; gh < G; ++gh) sl.q[gh] = load_chunk(qbase + ((size_t)b * Hq + gh) * D);
+    if constexpr (FUSED) {
+      sl.nk = load_chunk(nkbase + (size_t)b * tok_stride);
+      sl.nv = load_chunk(nvbase + (size_t)b * tok_stride);
+    }
+  };
+
+  Row st;
+  int seg_i = 0, seg_j = 0;
+  bool poisoned = false;
+  // Sequences whose partial state this worker leaves in slot 0 (the range
+  // starts inside them or they continue past its end) and slot 1 (the last
+  // sequence, when it started inside the range and continues past its end);
+  // -1 for none.  Wave-uniform, known from the range's first and last blocks.
+  int pend0, pend1;
+  {
+    const int v0 = w.seqblk(0), vl = w.seqblk(w.n - 1);
+    const int b0 = (v0 >> 16) & 0x7FFF, j0 = v0 & 0xFFFF;
+    const int bl = (vl >> 16) & 0x7FFF, jl = vl & 0xFFFF;
+    const int nb0 = (w.ctx(0) + BS - 1) / BS, nbl = (w.ctx(w.n - 1) + BS - 1) / BS;
+    const bool first_whole = j0 == 0 && nb0 - j0 <= w.n;
+    pend0 = first_whole ? -1 : b0;
+    pend1 = (bl != b0 && jl != nbl - 1) ? bl : -1;
+  }
+  // Where their pieces lie, worked out now rather than after the stream, when
+  // the merge is on the launch's critical path.
+  const SeqPieces sp0(s_cum[max(pend0, 0)], s_cum[max(pend0, 0) + 1] - s_cum[max(pend0, 0)], T, R);
+  const SeqPieces sp1(s_cum[max(pend1, 0)], s_cum[max(pend1, 0) + 1] - s_cum[max(pend1, 0)], T, R);
+  // The partial state of the range's first sequence, kept in registers until
+  // the range is done: a store issued in the middle of the stream would hold
+  // up the waits on every load issued after it (one in-order counter covers
+  // loads and stores), and a system-scope store takes a memory round trip.
+  float first_m[G], first_l[G], first_acc[G][E];
+
+  // Partial state of (this worker, slot) to the workspace, for the merge:
+  // the G rows of a piece are contiguous, G * D floats of output, then G
+  // (max, sum) pairs; a lane of row group `row` writes its E values of the
+  // query heads gh with gh % ROWS == row.
+  auto publish_state = [&](int slot, const float (&m)[G], const float (&l)[G],
+                           const float (&acc)[G][E]) {
+    const size_t pr0 = stream_piece_row(h, r, slot, 0, R, G);
+    const CoherentRegion racc(a.ws_acc + pr0 * D, G * D * 4);
+    const CoherentRegion rml(a.ws_ml + pr0 * 2, G * 2 * 4);
+#pragma unroll
+    for (int gh = 0; gh < G; ++gh) {
+      if (gh % ROWS == row) {
+        const uint32_t off = (gh * D + col * E) * 4;
+#pragma unroll
+        for (int e = 0; e < E; e += 4)
+          racc.store4(off + 4 * e, acc[gh][e], acc[gh][e + 1], acc[gh][e + 2], acc[gh][e + 3]);
+        if (col == 0) rml.store2(gh * 8, m[gh], l[gh]);
+      }
+    }
+  };
+
+  // End of the sequence's blocks held by this worker: the output rows when
+  // the worker held all of them, else the partial state for the merge (a
+  // NaN sum when a block of it lay outside the pool).
+  auto finish = [&](int b, int j, int nb) {
+    st.merge_rows();
+    if (seg_j == 0 && j == nb - 1) {
+#pragma unroll
+      for (int gh = 0; gh < G; ++gh) {
+        if (gh % ROWS == row) {
+          float x[E];
+#pragma unroll
+          for (int e = 0; e < E; ++e) x[e] = poisoned ? __builtin_nanf("") : st.acc[gh][e] / st.l[gh];
+          S* o = static_cast<S*>(a.out) + ((size_t)b * Hq + (size_t)h * G + gh) * D + col * E;
+          store_chunk(o, out_chunk(DT{}, x));
+        }
+      }
+    } else {
+      const int slot = seg_i > 0 ? 1 : 0;
+      float l[G];
+#pragma unroll
+      for (int gh = 0; gh < G; ++gh) l[gh] = poisoned ? __builtin_nanf("") : st.l[gh];
+      if (slot == 0) {
+#pragma unroll
+        for (int gh = 0; gh < G; ++gh) {
+          first_m[gh] = st.m[gh];
+          first_l[gh] = l[gh];
+#pragma unroll
+          for (int e = 0; e < E; ++e) first_acc[gh][e] = st.acc[gh][e];
+        }
+      } else {
+        // The range's last sequence: the range is done, publish at once.
+        publish_state(1, st.m, l, st.acc);
+      }
+
+    }
+  };
+
+  auto consume = [&](int i, Slot& sl) {
+    // Everything read back from the lanes (readlane) is read here, with every
+    // lane active: a value selected per lane inside a divergent branch is not
+    // defined in the inactive lanes readlane would read.
+    const int id = w.entry(i);
+    const int v = w.seqblk(i);
+    const int b = (v >> 16) & 0x7FFF, j = v & 0xFFFF;
+    const bool bad = v < 0;
+    const int ctx = w.ctx(i);
+    const int nb = (ctx + BS - 1) / BS;
+    if (i == 0 || j == 0) {
+      st.reset();
+      seg_i = i;
+      seg_j = j;
+      poisoned = false;
+    }
+    poisoned = poisoned || bad;
+    if constexpr (FUSED) {
+      if (j == nb - 1) {
+        // Position ctx - 1 (token t of this block) holds the step's token.
+        const int t = (ctx - 1) % BS;
+        const int li = t / ROWS, lr = t % ROWS;
+#pragma unroll
+        for (int ii = 0; ii < NI; ++ii) {
+          if (ii == li && row == lr) {
+            sl.k[ii] = sl.nk;
+            sl.v[ii] = sl.nv;
+          }
+        }
+        if (!bad && row == lr) {
+          const size_t dst =
+              (size_t)id * blk_stride + (size_t)t * tok_stride + (size_t)h * D + col * E;
+          store_chunk(static_cast<S*>(const_cast<void*>(a.k_cache)) + dst, sl.nk);
+          store_chunk(static_cast<S*>(const_cast<void*>(a.v_cache)) + dst, sl.nv);
+        }
+      }
+    }
+#pragma unroll
+    for (int gh = 0; gh < G; ++gh) st.qv[gh] = sl.q[gh];
+    st.consume(j * BS + row, ctx, !bad, a.scale_log2, sl.k, sl.v);
+    if (i == w.n - 1 || j == nb - 1) finish(b, j, nb);
+  };
+
+  Slot sl[PF];
+  const auto clampi = [&](int i) { return i < w.n ? i : w.n - 1; };
+#pragma unroll
+  for (int p = 0; p < PF - 1; ++p) {
+    fetch(clampi(p), sl[p]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int i0 = 0; i0 < w.n; i0 += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      fetch(clampi(i0 + u + PF - 1), sl[(u + PF - 1) % PF]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i0 + u < w.n) consume(i0 + u, sl[u]);
+    }
+  }
+
+  if (pend0 >= 0) publish_state(0, first_m, first_l, first_acc);
+  // Arrivals of the published states; the last worker of a sequence merges
+  // (or the merge kernel that follows, with deferred_merge).
+  if ((pend0 < 0 && pend1 < 0) || a.deferred_merge) return;
+  __builtin_amdgcn_s_waitcnt(0);  // every published store of this wave is complete
+  const int prev0 = pend0 >= 0 ? stream_arrive_issue(a.counters + (size_t)pend0 * Hkv + h, lane) : 0;
+  const int prev1 = pend1 >= 0 ? stream_arrive_issue(a.counters + (size_t)pend1 * Hkv + h, lane) : 0;
+  auto merge_if_last = [&](int b, int prev, const SeqPieces& sp) {
+    if (__builtin_amdgcn_readfirstlane(prev) != sp.count() - 1) return;
+    stream_merge<DT, D, G>(a, b, h, sp, R, lane);
+    if (lane == 0)
+      __hip_atomic_store(a.counters + (size_t)b * Hkv + h, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
+  };
+  if (pend0 >= 0) merge_if_last(pend0, prev0, sp0);
+  if (pend1 >= 0) merge_if_last(pend1, prev1, sp1);
+}
+
+// The merges of split sequences as a kernel of their own, launched right
+// after the stream kernel: one wave per (sequence, kv head), the prefix sum
+// recomputed by each workgroup.  The stream kernel's published states are
+// complete and visible once it has ended.
+template <class DT, int D, int G>
+__global__ __launch_bounds__(kStreamWaves * 64) void stream_merge_kernel(DecodeArgs a, int bs) {
+  __shared__ int s_cum[kStreamMaxSeqs + 1];
+  __shared__ int s_part[kStreamWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int T = stream_prefix<kStreamWaves * 64>(a, bs, s_cum, s_part, [](int, int) {});
+  const int R = min(a.stream_workers, T);
+  const int item = blockIdx.x * kStreamWaves + wave;
+  const int Hkv = a.num_kv_heads;
+  if (item >= a.num_seqs * Hkv) return;
+  const int b = item / Hkv, h = item % Hkv;
+  const int cb = s_cum[b], nb = s_cum[b + 1] - cb;
+  if (nb == 0) return;
+  const SeqPieces sp(cb, nb, T, R);
+  if (sp.count() > 1) stream_merge<DT, D, G>(a, b, h, sp, R, lane);
+}
+
+bool stream_supported(int G) { return G == 1 || G == 2 || G == 4; }
+
+hipError_t launch_stream_merge(int dtype, int D, int BS, int G, const DecodeArgs& a,
+                               hipStream_t s) {
+  const dim3 grid((unsigned)((a.num_seqs * a.num_kv_heads + kStreamWaves - 1) / kStreamWaves));
+  auto go = [&](auto dt, auto d, auto g) -> hipError_t {
+    stream_merge_kernel<decltype(dt), decltype(d)::value, decltype(g)::value>
+        <<<grid, kStreamWaves * 64, 0, s>>>(a, BS);
+    return hipGetLastError();
+  };
+  auto by_g = [&](auto dt, auto d) -> hipError_t {
+    switch (G) {
+      case 1: return go(dt, d, IntC<1>{});
+      case 2: return go(dt, d, IntC<2>{});
+      case 4: return go(dt, d, IntC<4>{});
+    }
+    return hipErrorInvalidValue;
+  };
+  auto by_d = [&](auto dt) -> hipError_t {
+    return D == 64 ? by_g(dt, IntC<64>{}) : by_g(dt, IntC<128>{});
+  };
+  return dtype == PA_DTYPE_BF16 ? by_d(BF16{}) : by_d(F32{});
+}
+
+hipError_t launch_stream(int dtype, int D, int BS, int G, const DecodeArgs& a, hipStream_t s) {
+  const int HW = stream_heads_per_wg(a.num_kv_heads);
+  const dim3 grid((unsigned)(a.num_kv_heads / HW * (a.stream_workers / (kStreamWaves / HW))));
+  const bool fused = a.new_k != nullptr;
+  auto go = [&](auto dt, auto d, auto bs, auto g) -> hipError_t {
+    using DT = decltype(dt);
+    constexpr int Dv = decltype(d)::value, BSv = decltype(bs)::value, Gv = decltype(g)::value;
+    if (fused)
+      decode_stream_kernel<DT, Dv, BSv, Gv, true><<<grid, kStreamWaves * 64, 0, s>>>(a);
+    else
+      decode_stream_kernel<DT, Dv, BSv, Gv, false><<<grid, kStreamWaves * 64, 0, s>>>(a);
+    return hipGetLastError();
+  };
+  auto by_g = [&](auto dt, auto d, auto bs) -> hipError_t {
+    switch (G) {
+      case 1: return go(dt, d, bs, IntC<1>{});
+      case 2: return go(dt, d, bs, IntC<2>{});
+      case 4: return go(dt, d, bs, IntC<4>{});
+    }
+    return hipErrorInvalidValue;
+  };
+  auto by_bs = [&](auto dt, auto d) -> hipError_t {
+    return BS == 16 ? by_g(dt, d, IntC<16>{}) : by_g(dt, d, IntC<32>{});
+  };
+  auto by_d = [&](auto dt) -> hipError_t {
+    return D == 64 ? by_bs(dt, IntC<64>{}) : by_bs(dt, IntC<128>{});
+  };
+  return dtype == PA_DTYPE_BF16 ? by_d(BF16{}) : by_d(F32{});
+}
+
+}  // namespace pa

@@ -26,6 +26,7 @@
 // There is no split over key ranges, so no workspace and no merge: each
 // wave's state ends complete and is normalised and stored directly.
 #include "mfma_tile32.hpp"
+#include "options.hpp"
 
 #include "decode_launch.hpp"
 
@@ -505,10 +506,7 @@ extern "C" pa_status pa_paged_attention_prefill(
   // table spans at least four times the longest query, i.e. few new rows
   // against long contexts.  PAGEDATTN_PREFILL_KSPLIT=1|2 forces either.
   int ks = (int64_t)max_blocks_per_seq * block_size >= 4 * (int64_t)max_query_len ? 2 : 1;
-  if (const char* env = getenv("PAGEDATTN_PREFILL_KSPLIT")) {
-    if (env[0] == '1') ks = 1;
-    if (env[0] == '2') ks = 2;
-  }
+  if (options().prefill_ksplit) ks = options().prefill_ksplit;
   const int64_t rows_per_wg = (int64_t)kPrefillWaves * kPrefillRows / ks;
   const int64_t row_groups = ((int64_t)max_query_len * G + rows_per_wg - 1) / rows_per_wg;
   // Workgroups are numbered blockIdx.y * gridDim.x + blockIdx.x in 32 bits.

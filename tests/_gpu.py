@@ -8,9 +8,17 @@ import numpy as np
 import torch
 
 import synth
+import paged_kv_cache_reshape_amd as pa
 
-# Tolerances: elementwise |y - y*| <= atol + rtol * |y*|.  bfloat16 inputs with
-# float32 accumulation: atol 2e-3, rtol 1e-2; float32 inputs: 1e-5 both.
+# Tolerances.  Every element: |y - y*| <= atol + rtol * |y*| (bfloat16 inputs
+# with float32 accumulation: atol 2e-3, rtol 1e-2; float32 inputs: 1e-5 both).
+# On top of it the stated maxima where the output's own rounding leaves room
+# for them: bfloat16 round-to-nearest-even costs at most half an ulp, 2^-10
+# below |y| = 0.5 and at most 2^-8 |y| anywhere, so max abs <= 2e-3 is asserted
+# over |y*| < 0.5 and max rel <= 1e-2 over |y*| >= 0.2 (float32: max abs <=
+# 1e-5 over |y*| < 0.5, max rel <= 1e-5 over |y*| >= 0.2 is not asserted --
+# near 0.2 it asks for 2e-6 absolute, below what float32 sums of thousands of
+# terms guarantee -- the elementwise bound stands there).
 TOL = {"bf16": (2e-3, 1e-2), "f32": (1e-5, 1e-5)}
 
 
@@ -52,15 +60,35 @@ def upload(inp: dict, device="cuda") -> dict:
     )
 
 
+LITERAL = {"bf16": (2e-3, 1e-2), "f32": (1e-5, None)}
+
+
 def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
+    """Elementwise bound, then the literal maxima where they apply; returns
+    (max abs error, max rel error over |y*| >= 0.2)."""
     atol, rtol = TOL[dtype]
     assert got.shape == ref.shape
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     err = np.abs(got - ref)
     bad = err > atol + rtol * np.abs(ref)
     big = np.abs(ref) >= 0.2
+    small = np.abs(ref) < 0.5
     max_rel = float((err[big] / np.abs(ref[big])).max()) if big.any() else 0.0
+    max_abs_small = float(err[small].max()) if small.any() else 0.0
     assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside "
                            f"{atol} + {rtol}|y|; max abs {err.max():.3g}, "
                            f"max rel {max_rel:.3g}")
+    lit_abs, lit_rel = LITERAL[dtype]
+    assert max_abs_small <= lit_abs, (f"{what}: max abs error {max_abs_small:.3g} over "
+                                      f"|y*| < 0.5 exceeds {lit_abs}")
+    if lit_rel is not None:
+        assert max_rel <= lit_rel, (f"{what}: max rel error {max_rel:.3g} over |y*| >= 0.2 "
+                                    f"exceeds {lit_rel}")
     return float(err.max()), max_rel
+
+
+def setopt(monkeypatch, name: str, value) -> None:
+    """Set a PAGEDATTN_* override for this test and make the library see it
+    (conftest re-reads the restored environment after the test)."""
+    monkeypatch.setenv(name, str(value))
+    pa.reload_options()

@@ -172,26 +172,51 @@ def test_partition_size_rule(lib):
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 64) == 1024
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 128) == 2048
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 129) == -1
-    # left to the library: 1024 tokens at head_dim 128; at head_dim 64, 512
-    # for groups of 1 or 2 query heads, 1024 for more
-    assert pa.decode_partition_size(32, 16, 8, 128, 128, 16, 0) == 1024
+    # left to the library: the balanced schedule (reported as 0) for 1 or 2
+    # query heads per kv head and at most 1024 (sequence, kv head) pairs;
+    # otherwise 1024 tokens at head_dim 128 (2048 for tables of more than
+    # 4096 tokens) and 1024 at head_dim 64 for groups of 4 or more
+    assert pa.decode_partition_size(32, 16, 8, 128, 128, 16, 0) == 0
+    assert pa.decode_partition_size(64, 16, 8, 64, 256, 16, 0) == 0
+    assert pa.decode_partition_size(4, 4, 2, 64, 4, 16, 0) == 0
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 0) == 2048
     assert pa.decode_partition_size(8, 32, 8, 128, 256, 16, 0) == 1024
     assert pa.decode_partition_size(8, 32, 8, 128, 257, 16, 0) == 2048
     assert pa.decode_partition_size(256, 32, 32, 128, 32, 32, 0) == 1024
     assert pa.decode_partition_size(64, 32, 8, 64, 256, 16, 0) == 1024
-    assert pa.decode_partition_size(64, 16, 8, 64, 256, 16, 0) == 512
-    assert pa.decode_partition_size(4, 4, 2, 64, 4, 16, 0) == 512
+    assert pa.decode_partition_size(600, 16, 8, 64, 256, 16, 0) == 512  # 4800 pairs
+
+
+def test_schedule_override_is_read_once_and_reloaded(lib, monkeypatch):
+    """PAGEDATTN_SCHEDULE takes effect after pa_reload_options, not before."""
+    monkeypatch.setenv("PAGEDATTN_SCHEDULE", "fixed")
+    assert pa.decode_partition_size(32, 16, 8, 128, 128, 16, 0) == 0  # not re-read yet
+    pa.reload_options()
+    assert pa.decode_partition_size(32, 16, 8, 128, 128, 16, 0) == 1024
+    monkeypatch.setenv("PAGEDATTN_SCHEDULE", "stream")
+    pa.reload_options()
+    assert pa.decode_partition_size(8, 32, 8, 128, 256, 16, 0) == 0
+    assert pa.decode_partition_size(8, 64, 8, 128, 256, 16, 0) == 1024  # G = 8: not built
 
 
 def test_workspace_size_rule(lib):
     def al(x):
         return (x + 255) // 256 * 256
-    # library choice for the Qwen3 shape: 1024-token partitions of a
-    # 2048-token table -> 2 partitions per sequence
+    # library choice for the Qwen3 shape: the balanced schedule, 128 workers
+    # per kv head (1024 in all), two partial states each of G rows
     B, Hq, Hkv, D, mb, bs = 32, 16, 8, 128, 128, 16
-    rows = B * Hkv * 2 * (Hq // Hkv)
+    rows = Hkv * 128 * 2 * (Hq // Hkv)
     assert pa.decode_workspace_bytes(B, Hq, Hkv, D, mb, bs, 0) == \
+        al(rows * D * 4) + al(rows * 2 * 4)
+    # the workers are enough that no range exceeds 128 blocks: 500 sequences
+    # of 2048-token tables need 8000 workers per kv head
+    rows = 2 * 8000 * 2 * 2
+    assert pa.decode_workspace_bytes(500, 4, 2, 128, 2048, 16, 0) == \
+        al(rows * 128 * 4) + al(rows * 2 * 4)
+    # with a fixed partition size: 1024-token partitions of a 2048-token
+    # table -> 2 partitions per sequence
+    rows = B * Hkv * 2 * (Hq // Hkv)
+    assert pa.decode_workspace_bytes(B, Hq, Hkv, D, mb, bs, 1024) == \
         al(rows * D * 4) + al(rows * 2 * 4)
     # no workspace when every sequence fits one partition
     assert pa.decode_workspace_bytes(4, 4, 2, 64, 4, 16, 64) == 0

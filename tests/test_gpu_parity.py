@@ -2,8 +2,10 @@
 
 Bit-exact: the KV write, the dense gather (block-table indexing), the
 single-token and hard-max closed forms, block relabelling, NaN poisoning,
-reruns.  Within tolerance (bf16: 2e-3 + 1e-2|y|; f32: 1e-5 + 1e-5|y|): every
-decode output against the oracle.
+reruns.  Within tolerance (tests/_gpu.py: bf16 2e-3 + 1e-2|y| elementwise, max
+abs 2e-3 below |y| = 0.5, max rel 1e-2 above |y| = 0.2; f32 1e-5 + 1e-5|y|):
+every decode output against the oracle -- the two-launch step, the fused step
+and graph replays of both.
 """
 import sys
 
@@ -155,7 +157,7 @@ def test_decode_matches_oracle(name):
                                   "llama32_1b", "bf16_d64_bs32_g4", "bf16_d128_bs16_g4"])
 def test_vector_alu_kernel_matches_oracle(name, monkeypatch):
     """The vector-ALU kernel on shapes the matrix-core kernel takes by default."""
-    monkeypatch.setenv("PAGEDATTN_DECODE_KERNEL", "valu")
+    G.setopt(monkeypatch, "PAGEDATTN_DECODE_KERNEL", "valu")
     inp = inputs_for(name)
     w = inp["workload"]
     say("write+decode (vector ALU kernel)", name)
@@ -180,17 +182,32 @@ def test_large_scores_match_oracle(name, factor):
     G.assert_close(out, ref, w.dtype, f"{name} scale x{factor}")
 
 
-def test_decode_long_split_k_sampled():
-    """32,768-token sequences, 512-token partitions (64 per sequence), merged
-    in the same launch; the oracle checks every head of three sequences."""
+@pytest.fixture(scope="module")
+def long_splitk_oracle():
+    """The oracle's write + decode of every sequence of the 32,768-token batch
+    (it gathers one sequence at a time, so each sequence's float64 rows are
+    freed before the next is read)."""
     inp = inputs_for("long_splitk")
+    ref, _ = oracle_step(inp)
+    return inp, ref
+
+
+@pytest.mark.parametrize("ps", [512, 0])
+def test_decode_long_split_k(long_splitk_oracle, ps):
+    """32,768-token sequences at 512-token partitions as stated (64 per
+    sequence) and at the library's choice: split sequences of 16 or more
+    partitions are merged by the merge kernel that follows the partition
+    launch.  Every output row of all eight sequences against the oracle."""
+    inp, ref = long_splitk_oracle
     w = inp["workload"]
-    say("write+decode long_splitk partition", w.partition_size)
+    say("write+decode long_splitk partition", ps or "library choice")
     d = G.upload(inp)
-    out = G.host_f64(gpu_step(d, w.partition_size))
-    seqs = [0, 3, 7]
-    ref, _ = oracle_step(inp, seqs)
-    G.assert_close(out[seqs], ref, w.dtype, "long_splitk")
+    out = G.host_f64(gpu_step(d, ps))
+    G.assert_close(out, ref, w.dtype, f"long_splitk ps={ps}")
+    # The fused step, the launch the benchmark times, on fresh caches.
+    d2 = G.upload(inp)
+    got = G.host_f64(fused_step(d2, ps))
+    G.assert_close(got, ref, w.dtype, f"long_splitk fused step ps={ps}")
 
 
 @pytest.mark.parametrize("merge", ["inkernel", "separate"])
@@ -200,7 +217,7 @@ def test_decode_long_split_k_sampled():
 def test_merge_paths_match_oracle(name, ps, merge, monkeypatch):
     """Split sequences merged by the last partition workgroup to arrive, or by
     the merge kernel that follows the partition launch."""
-    monkeypatch.setenv("PAGEDATTN_MERGE", merge)
+    G.setopt(monkeypatch, "PAGEDATTN_MERGE", merge)
     inp = inputs_for(name)
     w = inp["workload"]
     say("write+decode", name, "partition", ps, "merge", merge)
@@ -219,7 +236,7 @@ def test_heads_per_workgroup_match_oracle(name, ps, hpw, merge, monkeypatch):
     the last partition to arrive (every kv head of its group in one pass, a
     separate code path for each group size) or by the merge kernel."""
     monkeypatch.setenv("PAGEDATTN_HEADS_PER_WG", str(hpw))
-    monkeypatch.setenv("PAGEDATTN_MERGE", merge)
+    G.setopt(monkeypatch, "PAGEDATTN_MERGE", merge)
     inp = inputs_for(name)
     w = inp["workload"]
     say("write+decode", name, "partition", ps, "heads per workgroup", hpw, "merge", merge)
@@ -254,7 +271,7 @@ def test_vector_kernel_every_shape(dtype, D, bs, G_, monkeypatch):
     """Every (dtype, head_dim, block size, group) the vector-ALU kernel is
     built for (forced where the matrix cores would take the shape), on a
     small ragged batch that splits its longer sequences."""
-    monkeypatch.setenv("PAGEDATTN_DECODE_KERNEL", "valu")
+    G.setopt(monkeypatch, "PAGEDATTN_DECODE_KERNEL", "valu")
     hkv = 2 if G_ <= 16 else 1
     w = synth.Workload(f"valu_{dtype}_d{D}_bs{bs}_g{G_}", 4, G_ * hkv, hkv, D, bs, dtype,
                        ("uniform", 1, 600), seed=60 + D + bs + G_)
@@ -277,15 +294,17 @@ def test_partition_sizes_agree(ps):
 
 
 def test_max_context_everywhere():
-    """Every sequence fills its whole table (2048 tokens = 128 blocks)."""
+    """Every sequence fills its whole table (2048 tokens = 128 blocks); every
+    row of all 32 sequences against the oracle."""
     w = synth.WORKLOADS["qwen3_0p6b"]
     inp = synth.make_inputs(w, context_lens=np.full(w.num_seqs, 2048, np.int32))
     say("decode qwen3 ctx=2048 all")
     d = G.upload(inp)
     out = G.host_f64(gpu_step(d))
-    seqs = [0, 13, 31]
-    ref, _ = oracle_step(inp, seqs)
-    G.assert_close(out[seqs], ref, "bf16", "max ctx")
+    ref, _ = oracle_step(inp)
+    G.assert_close(out, ref, "bf16", "max ctx")
+    d2 = G.upload(inp)
+    G.assert_close(G.host_f64(fused_step(d2)), ref, "bf16", "max ctx fused step")
 
 
 @pytest.mark.parametrize("name", ["tiny_f32", "qwen3_0p6b", "bf16_d64_bs32_g8",
@@ -410,7 +429,7 @@ def test_bad_table_entries_give_nan_rows_only(name, ps, merge, monkeypatch):
     dereferenced: that sequence's rows become NaN, the others are unchanged
     (with split sequences merged in the partition kernel or after it; the
     vector-ALU kernel and the matrix-core one)."""
-    monkeypatch.setenv("PAGEDATTN_MERGE", merge)
+    G.setopt(monkeypatch, "PAGEDATTN_MERGE", merge)
     inp = inputs_for(name)
     w = inp["workload"]
     B, bs = w.num_seqs, w.block_size
@@ -451,10 +470,16 @@ def test_decode_step_equals_write_then_decode(name, ps):
     say("fused step", name, ps)
     d1, d2 = G.upload(inp), G.upload(inp)
     want = G.host_storage(gpu_step(d1, ps))
-    got = G.host_storage(fused_step(d2, ps))
+    got_dev = fused_step(d2, ps)
+    got = G.host_storage(got_dev)
     assert np.array_equal(got, want)
     for c in ("k_cache", "v_cache"):
         assert torch.equal(d1[c], d2[c]), c
+    # And against the oracle directly: its write, then its decode.
+    ref, (k_ref, v_ref) = oracle_step(inp)
+    G.assert_close(G.host_f64(got_dev), ref, inp["workload"].dtype, f"fused step {name}")
+    assert np.array_equal(G.host_storage(d2["k_cache"]), k_ref)
+    assert np.array_equal(G.host_storage(d2["v_cache"]), v_ref)
 
 
 def test_decode_step_edge_sequences():
@@ -510,7 +535,7 @@ def test_one_counter_array_serves_every_geometry(monkeypatch):
     """Counters left at zero by each call: alternate two geometries whose
     partial results overlap differently, with one shared counter array
     (merged in the partition kernel, the path that counts arrivals)."""
-    monkeypatch.setenv("PAGEDATTN_MERGE", "inkernel")
+    G.setopt(monkeypatch, "PAGEDATTN_MERGE", "inkernel")
     cnt = torch.zeros(4096, dtype=torch.int32, device="cuda")
     cases = [("qwen3_0p6b", 64), ("bf16_d128_bs16_g16", 32), ("llama32_1b", 128),
              ("qwen3_0p6b", 32)]
@@ -530,6 +555,160 @@ def test_one_counter_array_serves_every_geometry(monkeypatch):
         ref, _ = oracle_step(inp)
         G.assert_close(G.host_f64(out), ref, w.dtype, f"{name} ps={ps}")
         assert int(cnt.abs().sum()) == 0
+
+
+# ------------------------------------------------------------------ stream schedule
+def stream_case(dtype, D, bs, G_, hkv=2, B=9, top=900, seed=0, empty=True):
+    w = synth.Workload(f"stream_{dtype}_d{D}_bs{bs}_g{G_}_{seed}", B, G_ * hkv, hkv, D, bs,
+                       dtype, ("uniform", 1, top), seed=500 + seed + D + bs + G_)
+    inp = synth.make_inputs(w)
+    if empty:
+        ctx = inp["context_lens"].copy()
+        ctx[::4] = [0, 1, 17][: len(ctx[::4])] + [1] * max(0, len(ctx[::4]) - 3)
+        inp = synth.make_inputs(w, context_lens=ctx)
+    return inp
+
+
+def check_stream(inp, what):
+    """Write + decode and the fused step against the oracle; the two agree
+    bit for bit (output and caches)."""
+    w = inp["workload"]
+    d1, d2 = G.upload(inp), G.upload(inp)
+    out = gpu_step(d1)
+    ref, (k_ref, v_ref) = oracle_step(inp)
+    G.assert_close(G.host_f64(out), ref, w.dtype, what)
+    got = fused_step(d2)
+    assert np.array_equal(G.host_storage(got), G.host_storage(out)), what
+    assert torch.equal(d1["k_cache"], d2["k_cache"]) and torch.equal(d1["v_cache"], d2["v_cache"])
+    assert np.array_equal(G.host_storage(d2["k_cache"]), k_ref)
+    return out
+
+
+@pytest.mark.parametrize("workers", [8, 64, 1024])
+@pytest.mark.parametrize("G_", [1, 2, 4])
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_stream_schedule_every_shape(dtype, D, bs, G_, workers, monkeypatch):
+    """The balanced schedule on every (dtype, head_dim, block size, group) it
+    is built for, on a ragged batch with empty and one-token sequences: with
+    few workers (ranges of up to 128 blocks, many sequences each), some, and
+    many (sequences split over many workers, merged by the last to finish)."""
+    G.setopt(monkeypatch, "PAGEDATTN_SCHEDULE", "stream")
+    G.setopt(monkeypatch, "PAGEDATTN_STREAM_WORKERS", workers)
+    inp = stream_case(dtype, D, bs, G_)
+    say("stream", inp["workload"].name, "workers", workers)
+    check_stream(inp, f"stream {inp['workload'].name} workers={workers}")
+
+
+@pytest.mark.parametrize("merge", ["separate", "inkernel"])
+@pytest.mark.parametrize("shape", [("bf16", 128, 16, 2, 64), ("f32", 64, 32, 1, 8),
+                                   ("bf16", 64, 32, 4, 1024), ("bf16", 128, 16, 2, 4096)])
+def test_stream_merge_paths(shape, merge, monkeypatch):
+    """Split sequences of the balanced schedule merged by the last worker to
+    finish, or by the merge kernel launched after the stream kernel."""
+    dtype, D, bs, G_, workers = shape
+    G.setopt(monkeypatch, "PAGEDATTN_SCHEDULE", "stream")
+    G.setopt(monkeypatch, "PAGEDATTN_STREAM_WORKERS", workers)
+    G.setopt(monkeypatch, "PAGEDATTN_MERGE", merge)
+    inp = stream_case(dtype, D, bs, G_, seed=3)
+    say("stream merge", merge, inp["workload"].name, "workers", workers)
+    check_stream(inp, f"stream merge={merge} {inp['workload'].name}")
+
+
+def test_stream_one_long_sequence_many_pieces(monkeypatch):
+    """A 4096-token sequence among short ones, 2048 workers per kv head: it
+    splits into dozens of pieces (merged four at a time)."""
+    G.setopt(monkeypatch, "PAGEDATTN_SCHEDULE", "stream")
+    G.setopt(monkeypatch, "PAGEDATTN_STREAM_WORKERS", 4096)
+    w = synth.Workload("stream_long_one", 6, 16, 8, 128, 16, "bf16", ("uniform", 1, 4096),
+                       seed=71)
+    ctx = np.array([4096, 3, 200, 1, 0, 77], dtype=np.int32)
+    inp = synth.make_inputs(w, context_lens=ctx)
+    say("stream one long sequence")
+    check_stream(inp, "stream long one")
+
+
+def test_stream_many_short_sequences(monkeypatch):
+    """2000 sequences of 0-16 tokens, 16 workers per kv head: a worker's range
+    spans more than 64 sequences (the range set-up walks the sequence starts
+    in chunks of 64)."""
+    G.setopt(monkeypatch, "PAGEDATTN_SCHEDULE", "stream")
+    G.setopt(monkeypatch, "PAGEDATTN_STREAM_WORKERS", 32)
+    w = synth.Workload("stream_many_short", 2000, 4, 2, 64, 16, "bf16", ("uniform", 0, 16),
+                       seed=72)
+    inp = synth.make_inputs(w)
+    say("stream 2000 short sequences")
+    check_stream(inp, "stream many short")
+
+
+def test_stream_library_choice_on_qwen3_shape():
+    """The library's own choice for the Qwen3-shaped batch is the balanced
+    schedule (reported as partition size 0), and its result is the oracle's."""
+    w = synth.WORKLOADS["qwen3_0p6b"]
+    assert pa.decode_partition_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                    w.max_blocks_per_seq, w.block_size, 0) == 0
+    say("stream qwen3 library choice")
+    check_stream(inputs_for("qwen3_0p6b"), "stream qwen3")
+
+
+def test_stream_bad_table_entries(monkeypatch):
+    """Block ids outside the pool on the balanced schedule: those sequences'
+    rows are NaN, nothing is dereferenced, every other row keeps its bits
+    (the lengths, hence the ranges, are unchanged); a length past the table
+    gives NaN rows too."""
+    G.setopt(monkeypatch, "PAGEDATTN_SCHEDULE", "stream")
+    inp = inputs_for("qwen3_0p6b")
+    w = inp["workload"]
+    B, bs = w.num_seqs, w.block_size
+    say("stream bad table entries")
+    d = G.upload(inp)
+    base = G.host_storage(gpu_step(d))
+    t = inp["block_tables"].copy()
+    ctx = inp["context_lens"].copy()
+    bad = [2, B // 2 + 1, B - 2]
+    t[bad[0], 0] = inp["num_blocks"]
+    t[bad[1], (ctx[bad[1]] - 1) // bs] = -5
+    t[bad[2], (ctx[bad[2]] - 1) // (2 * bs)] = inp["num_blocks"] + 100
+    d2 = dict(d, block_tables=torch.from_numpy(t).cuda())
+    out = gpu_step(d2, write=False)
+    assert np.all(np.isnan(G.host_f64(out)[bad]))
+    keep = [b for b in range(B) if b not in bad]
+    assert np.array_equal(G.host_storage(out)[keep], base[keep])
+    ctx2 = ctx.copy()
+    ctx2[5] = (t.shape[1] + 1) * bs
+    d3 = dict(d, context_lens=torch.from_numpy(ctx2).cuda())
+    got = G.host_f64(gpu_step(d3, write=False))
+    assert np.all(np.isnan(got[5]))
+    inp2 = dict(inp, context_lens=ctx2)
+    k, v = G.host_storage(d["k_cache"]), G.host_storage(d["v_cache"])
+    keep = [b for b in range(B) if b != 5]
+    ref = oracle.decode(inp["q"][keep], k, v, inp["block_tables"][keep], ctx2[keep],
+                        inp["scale"], "bf16")
+    G.assert_close(got[keep], ref, "bf16", "stream, one length past the table")
+
+
+def test_stream_rerun_bit_identical_and_counters_zero(monkeypatch):
+    """Reruns give the same bits whatever order the workers finish in, and
+    every call leaves the arrival counters at zero."""
+    G.setopt(monkeypatch, "PAGEDATTN_STREAM_WORKERS", 2048)
+    inp = inputs_for("qwen3_0p6b")
+    w = inp["workload"]
+    say("stream rerun")
+    d = G.upload(inp)
+    cnt = torch.zeros(w.num_seqs * w.num_kv_heads, dtype=torch.int32, device="cuda")
+    need = pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                     inp["max_blocks"], w.block_size, 0)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(4):
+        outs.append(G.host_storage(pa.decode_step(
+            d["q"], d["key"], d["value"], d["k_cache"], d["v_cache"], d["block_tables"],
+            d["context_lens"], d["scale"], workspace=ws, counters=cnt)))
+        torch.cuda.synchronize()
+        assert int(cnt.abs().sum()) == 0
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
 
 
 # ------------------------------------------------------------------ shared blocks
@@ -587,17 +766,21 @@ def test_prefix_fork_copy_on_write():
 
 
 # ------------------------------------------------------------------ graph capture
-@pytest.mark.parametrize("name,ps,fused", [("qwen3_0p6b", None, False), ("mqa_large", None, False),
-                                           ("qwen3_0p6b", 64, False), ("qwen3_0p6b", None, True),
-                                           ("qwen3_0p6b", 64, True)])
-def test_graph_replays_match_eager(name, ps, fused):
+@pytest.mark.parametrize("name,ps,fused,merge", [
+    ("qwen3_0p6b", None, False, None), ("mqa_large", None, False, None),
+    ("qwen3_0p6b", 64, False, None), ("qwen3_0p6b", None, True, None),
+    ("qwen3_0p6b", 64, True, None), ("qwen3_0p6b", None, True, "separate")])
+def test_graph_replays_match_eager(name, ps, fused, merge, monkeypatch):
     """A step (KV write + decode, or the fused step) captured in a HIP graph:
     every replay, with eager launches and host synchronisations between
     replays, gives the eager result bit for bit.  The workspace and the
     arrival counters are allocated before capture and passed in, so nothing
     is allocated or cleared inside the graph (the kernels leave the counters
     at zero themselves).  At 64-token partitions the step holds the separate
-    merge kernel too."""
+    merge kernel too, and with merge="separate" the balanced schedule's merge
+    kernel."""
+    if merge:
+        G.setopt(monkeypatch, "PAGEDATTN_MERGE", merge)
     inp = inputs_for(name)
     w = inp["workload"]
     say("graph capture", name, ps, "fused" if fused else "")
@@ -636,13 +819,19 @@ def test_graph_replays_match_eager(name, ps, fused):
     with torch.cuda.graph(g):
         step(graphed)
     scratch = torch.empty_like(d["q"])
+    ref, (k_ref, v_ref) = oracle_step(inp)
     for r in range(4):
         graphed.fill_(float("nan"))
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(G.host_storage(graphed), expect), f"replay {r}"
+        # Each replay against the oracle directly (the write is idempotent:
+        # every replay writes the same rows to the same slots).
+        G.assert_close(G.host_f64(graphed), ref, w.dtype, f"graph replay {r}")
         step(scratch)                    # eager work between replays
         torch.cuda.synchronize()
+    assert np.array_equal(G.host_storage(d["k_cache"]), k_ref)
+    assert np.array_equal(G.host_storage(d["v_cache"]), v_ref)
     assert int(cnt.abs().sum()) == 0
 
 
@@ -706,7 +895,7 @@ def prefill_oracle(inp):
 def test_prefill_matches_oracle(name, ks, monkeypatch):
     """Every prefill shape, with each wave folding all of its keys (1) and
     with the keys split between two waves per row set (2)."""
-    monkeypatch.setenv("PAGEDATTN_PREFILL_KSPLIT", ks)
+    G.setopt(monkeypatch, "PAGEDATTN_PREFILL_KSPLIT", ks)
     w = PF[name]
     inp = synth.make_prefill_inputs(w)
     say("prefill", name, "key halves", ks, "rows",
@@ -724,7 +913,7 @@ def test_prefill_matches_oracle(name, ks, monkeypatch):
 def test_prefill_every_shape(D, bs, G_, ks, monkeypatch):
     """Every (head_dim, block size, group) the prefill kernel is built for,
     in both forms, on chunks after cached prefixes (small ragged batch)."""
-    monkeypatch.setenv("PAGEDATTN_PREFILL_KSPLIT", ks)
+    G.setopt(monkeypatch, "PAGEDATTN_PREFILL_KSPLIT", ks)
     hkv = 2 if G_ <= 16 else 1
     w = synth.Workload(f"pf_d{D}_bs{bs}_g{G_}", 2, G_ * hkv, hkv, D, bs, "bf16",
                        ("uniform", 40, 300), seed=80 + D + bs + G_, query=("uniform", 1, 200))
@@ -739,7 +928,7 @@ def test_prefill_every_shape(D, bs, G_, ks, monkeypatch):
 def test_prefill_ragged_with_empty_and_bad_sequences(ks, monkeypatch):
     """A sequence with no new tokens writes nothing; a sequence claiming more
     new tokens than positions gets NaN rows; the others are unaffected."""
-    monkeypatch.setenv("PAGEDATTN_PREFILL_KSPLIT", ks)
+    G.setopt(monkeypatch, "PAGEDATTN_PREFILL_KSPLIT", ks)
     w = PF["pf_g2_d128_bs16"]
     inp = synth.make_prefill_inputs(w, query_lens=np.array([37, 0, 250, 5], dtype=np.int32))
     ctx = inp["context_lens"].copy()
