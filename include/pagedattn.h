@@ -282,6 +282,36 @@ pa_status pa_decode_step(void* out, const void* q, const void* key, const void* 
                          int64_t num_counters, pa_dtype dtype, void* stream);
 
 /*
+ * pa_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc): the
+ * same kernels, the same results bit for bit, with the split-K workspace and
+ * the arrival counters taken from a buffer the library keeps in static
+ * device memory -- 65536 counters and 16 MiB of workspace per GPU, held
+ * until the process ends.  Sizes that need more (num_seqs * num_kv_heads
+ * above 65536, or pa_decode_workspace_bytes(...) above 16 MiB) return
+ * PA_ERR_WORKSPACE_TOO_SMALL before anything is launched.  Nothing is
+ * allocated: the caller passes every input and `out`.
+ *
+ * The device of `stream` must be current.  The first call on a device finds
+ * that device's buffer and clears its counters with a kernel on `stream`; it
+ * must not be made under graph capture (PA_ERR_INVALID_ARGUMENT).  Every call
+ * on one GPU shares that GPU's buffer, which keeps the last call's contents:
+ * calls that may overlap on one GPU (other streams, other host threads) race
+ * and must be serialised by the caller.
+ *
+ * Arguments as for pa_decode_step, without workspace and counters.
+ */
+pa_status pa_decode_step_noalloc(void* out, const void* q, const void* key,
+                                 const void* value, void* k_cache, void* v_cache,
+                                 const int32_t* block_tables,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t num_blocks,
+                                 int32_t block_size, int32_t max_blocks_per_seq,
+                                 float scale, int32_t partition_size, pa_dtype dtype,
+                                 void* stream);
+
+/*
  * Test and debugging aid: the exact gather a dense-attention engine would do
  * (barellm README, feature list: pages gathered into dense tensors).
  *

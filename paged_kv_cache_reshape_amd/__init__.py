@@ -11,6 +11,9 @@ Functions (names follow the C ABI in ``include/pagedattn.h``):
                          scale, partition_size=0, out=None, workspace=None)
   decode_step(q, key, value, k_cache, v_cache, block_tables, context_lens,
               scale, ...)   the write of each sequence's new token fused in
+  decode_step_noalloc(q, key, value, k_cache, v_cache, block_tables,
+                      context_lens, scale, out, partition_size=0)
+                    the same with the library's own device buffer: no allocation
   paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens,
                           query_start, scale, max_query_len=None, out=None)
   copy_blocks(k_cache, v_cache, block_pairs)
@@ -32,7 +35,7 @@ __all__ = [
     "LIB_PATH", "load_library", "PagedAttnError", "reshape_and_cache",
     "paged_attention_decode", "decode_step", "paged_attention_prefill", "copy_blocks",
     "decode_partition_size", "decode_workspace_bytes", "debug_gather_kv", "workspace_for",
-    "counters_for", "reload_options",
+    "counters_for", "reload_options", "decode_step_noalloc",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
@@ -90,6 +93,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.pa_decode_step.argtypes = [
             vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
             vp, sz, vp, i64, i32, vp]
+        lib.pa_decode_step_noalloc.restype = i32
+        lib.pa_decode_step_noalloc.argtypes = [
+            vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+            i32, vp]
         lib.pa_paged_attention_prefill.restype = i32
         lib.pa_paged_attention_prefill.argtypes = [
             vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32,
@@ -242,9 +249,10 @@ def counters_for(device: torch.device, count: int, stream: int | None = None) ->
 
 
 def _decode_call(q, k_cache, v_cache, block_tables, context_lens, scale, partition_size,
-                 out, workspace, counters, step):
-    """Checks and buffers shared by the two decode entry points; `step` is
-    None or the (key, value) rows to write."""
+                 out, workspace, counters, step, noalloc=False):
+    """Checks and buffers shared by the decode entry points; `step` is None or
+    the (key, value) rows to write; `noalloc` calls pa_decode_step_noalloc
+    (no workspace, no counters, `out` given)."""
     lib = load_library()
     extra = step if step is not None else ()
     dev = _same_device(q, k_cache, v_cache, block_tables, context_lens, *extra)
@@ -271,8 +279,17 @@ def _decode_call(q, k_cache, v_cache, block_tables, context_lens, scale, partiti
     else:
         _same_device(out)
         _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
-    need = decode_workspace_bytes(B, hq, hkv, d, max_blocks, bs, partition_size)
     stream = _stream(dev)
+    if noalloc:
+        with _on(dev):
+            st = lib.pa_decode_step_noalloc(
+                out.data_ptr(), q.data_ptr(), key.data_ptr(), value.data_ptr(),
+                k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                context_lens.data_ptr(), B, hq, hkv, d, nb, bs, max_blocks, float(scale),
+                partition_size, dt, stream)
+        _check(st, "pa_decode_step_noalloc")
+        return out
+    need = decode_workspace_bytes(B, hq, hkv, d, max_blocks, bs, partition_size)
     if workspace is None:
         workspace = workspace_for(dev, need, stream)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -328,6 +345,19 @@ def decode_step(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
     :func:`paged_attention_decode`."""
     return _decode_call(q, k_cache, v_cache, block_tables, context_lens, scale, partition_size,
                         out, workspace, counters, (key, value))
+
+
+def decode_step_noalloc(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                        k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        block_tables: torch.Tensor, context_lens: torch.Tensor,
+                        scale: float, out: torch.Tensor,
+                        partition_size: int = 0) -> torch.Tensor:
+    """:func:`decode_step` through ``pa_decode_step_noalloc``: no workspace or
+    counters are allocated (the library's static device buffer serves, one
+    per GPU, shared by every call on it), and ``out`` is the caller's."""
+    _need(out is not None, "decode_step_noalloc writes into the caller's out")
+    return _decode_call(q, k_cache, v_cache, block_tables, context_lens, scale, partition_size,
+                        out, None, None, (key, value), noalloc=True)
 
 
 def paged_attention_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

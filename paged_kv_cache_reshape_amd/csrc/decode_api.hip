@@ -19,6 +19,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 namespace pa {
 namespace {
@@ -186,7 +187,74 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
   return p.total;
 }
 
+// Device memory of the entry point that allocates nothing
+// (pa_decode_step_noalloc): kScratchCounters arrival counters, then up to
+// kScratchWorkspaceBytes of split-K workspace.  Each GPU the library runs on
+// holds its own copy until the process ends; every call on that GPU shares
+// it.  In host code `scratch` names a host-side stand-in, never the device
+// memory: kernels and copies get the address hipGetSymbolAddress gives for
+// the current device (scratch_on_current_device).
+constexpr int64_t kScratchCounters = 65536;
+constexpr size_t kScratchCounterBytes = kScratchCounters * sizeof(int32_t);
+constexpr size_t kScratchWorkspaceBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char
+    scratch[kScratchCounterBytes + kScratchWorkspaceBytes];
+
 namespace {
+
+__global__ void __launch_bounds__(256) zero_counters(int32_t* c, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) c[i] = 0;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+char* g_scratch[kMaxDevices];  // per device: the address of its `scratch`
+
+// The current device's `scratch`.  The first call on a device looks the
+// address up and clears the counters with a fill kernel on `s` (a kernel,
+// not a memset, so that the clear is an ordinary stream operation); that
+// call must not be captured into a graph, since the graph's replays would be
+// the only runs of the clear.
+pa_status scratch_on_current_device(hipStream_t s, char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    set_error("no usable current device (%s, device %d)", hipGetErrorString(e), dev);
+    return PA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(s, &cs);
+    if (e != hipSuccess) {
+      set_error("stream query failed: %s", hipGetErrorString(e));
+      return PA_ERR_HIP;
+    }
+    if (cs != hipStreamCaptureStatusNone) {
+      set_error("the first pa_decode_step_noalloc call on device %d is under graph "
+                "capture; make one call outside capture first", dev);
+      return PA_ERR_INVALID_ARGUMENT;
+    }
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      set_error("hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                hipGetErrorString(e));
+      return PA_ERR_HIP;
+    }
+    zero_counters<<<dim3((unsigned)(kScratchCounters / 256)), dim3(256), 0, s>>>(
+        static_cast<int32_t*>(p), (int)kScratchCounters);
+    e = hipGetLastError();
+    if (e != hipSuccess) {
+      set_error("clearing the scratch counters failed: %s", hipGetErrorString(e));
+      return PA_ERR_HIP;
+    }
+    g_scratch[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch[dev];
+  return PA_OK;
+}
 
 // Both decode entry points: with `step`, the step's token rows key / value
 // are written into the caches by the decode launch itself.
@@ -196,7 +264,8 @@ pa_status decode_impl(void* out, const void* q, bool step, const void* key, cons
                       int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                       int32_t block_size, int32_t max_blocks_per_seq, float scale,
                       int32_t partition_size, void* workspace, size_t workspace_bytes,
-                      int32_t* counters, int64_t num_counters, pa_dtype dtype, void* stream) {
+                      int32_t* counters, int64_t num_counters, pa_dtype dtype, void* stream,
+                      bool own_scratch = false) {
   clear_error();
   if (!supported_dtype(dtype)) {
     set_error("dtype %d is not PA_DTYPE_F32 or PA_DTYPE_BF16", (int)dtype);
@@ -261,6 +330,27 @@ pa_status decode_impl(void* out, const void* q, bool step, const void* key, cons
     set_error("key and value must be non-NULL and 16-byte aligned");
     return PA_ERR_INVALID_ARGUMENT;
   }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (own_scratch && plan.total > 0) {
+    if (plan.total > kScratchWorkspaceBytes) {
+      set_error("these sizes need %zu bytes of workspace; pa_decode_step_noalloc holds "
+                "at most %zu (use pa_decode_step with a workspace)", plan.total,
+                kScratchWorkspaceBytes);
+      return PA_ERR_WORKSPACE_TOO_SMALL;
+    }
+    if ((int64_t)num_seqs * num_kv_heads > kScratchCounters) {
+      set_error("num_seqs * num_kv_heads = %lld; pa_decode_step_noalloc holds %lld "
+                "counters", (long long)num_seqs * num_kv_heads, (long long)kScratchCounters);
+      return PA_ERR_WORKSPACE_TOO_SMALL;
+    }
+    char* base = nullptr;
+    const pa_status st = scratch_on_current_device(s, &base);
+    if (st != PA_OK) return st;
+    counters = reinterpret_cast<int32_t*>(base);
+    num_counters = kScratchCounters;
+    workspace = base + kScratchCounterBytes;
+    workspace_bytes = kScratchWorkspaceBytes;
+  }
   if (plan.total > 0) {
     if (workspace_bytes < plan.total) {
       set_error("workspace holds %zu bytes, needs %zu", workspace_bytes, plan.total);
@@ -307,7 +397,6 @@ pa_status decode_impl(void* out, const void* q, bool step, const void* key, cons
   a.new_k = step ? key : nullptr;
   a.new_v = step ? value : nullptr;
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t err = plan.stream ? launch_stream(dtype, head_dim, block_size, G, a, s)
                          : mfma      ? launch_mfma(head_dim, block_size, G, a, s)
                                      : launch_partition(dtype, head_dim, block_size, G, a, s);
@@ -353,4 +442,16 @@ extern "C" pa_status pa_decode_step(
                      num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
                      max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes,
                      counters, num_counters, dtype, stream);
+}
+
+extern "C" pa_status pa_decode_step_noalloc(
+    void* out, const void* q, const void* key, const void* value, void* k_cache,
+    void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq, float scale,
+    int32_t partition_size, pa_dtype dtype, void* stream) {
+  return decode_impl(out, q, true, key, value, k_cache, v_cache, block_tables, context_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                     max_blocks_per_seq, scale, partition_size, nullptr, 0, nullptr, 0, dtype,
+                     stream, true);
 }

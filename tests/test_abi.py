@@ -110,6 +110,37 @@ def test_decode_step_argument_checks(lib, kw, status):
         assert lib.pa_last_error_message() != b""
 
 
+def _noalloc(lib, **kw):
+    a = dict(out=16, q=16, key=16, value=16, k=16, v=16, bt=16, cl=16, B=4, Hq=4, Hkv=2, D=64,
+             nb=32, bs=16, mb=4, scale=0.125, ps=0, dt=0)
+    a.update(kw)
+    return lib.pa_decode_step_noalloc(
+        a["out"], a["q"], a["key"], a["value"], a["k"], a["v"], a["bt"], a["cl"], a["B"],
+        a["Hq"], a["Hkv"], a["D"], a["nb"], a["bs"], a["mb"], a["scale"], a["ps"], a["dt"],
+        None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(key=None), INVALID),
+    (dict(dt=5), INVALID),
+    (dict(Hq=12, Hkv=4), UNSUPPORTED),
+    # The 32K-token batch at 512-token partitions needs 8 MiB + 128 KiB of
+    # workspace (fits); twice the table needs more than the 16 MiB held.
+    (dict(B=8, Hq=32, Hkv=8, D=128, mb=4096, ps=512, dt=1), WS_SMALL),
+    (dict(B=256, Hq=32, Hkv=32, D=128, mb=64, ps=128, dt=1), WS_SMALL),
+    (dict(B=0, q=None, out=None, key=None, value=None), OK),  # empty batch
+])
+def test_noalloc_step_rejects_before_launch(lib, kw, status):
+    """The entry point without allocation: its own size limit and the checks
+    it shares with pa_decode_step, all decided before any device call."""
+    assert _noalloc(lib, **kw) == status
+    if status:
+        msg = lib.pa_last_error_message()
+        assert msg != b""
+        if status == WS_SMALL:
+            assert b"noalloc" in msg
+
+
 def test_write_argument_checks(lib):
     f = lib.pa_reshape_and_cache
     assert f(16, 16, 16, 16, 16, 0, 2, 64, 32, 16, 0, None) == OK  # no tokens
@@ -254,6 +285,8 @@ def test_one_hip_runtime_in_process(lib):
 def test_ctypes_signatures_match_header(lib):
     assert lib.pa_decode_workspace_bytes.restype is ctypes.c_size_t
     assert len(lib.pa_paged_attention_decode.argtypes) == 21
+    assert len(lib.pa_decode_step.argtypes) == 23
+    assert len(lib.pa_decode_step_noalloc.argtypes) == 19
     assert len(lib.pa_reshape_and_cache.argtypes) == 12
     assert len(lib.pa_debug_gather_kv.argtypes) == 14
     assert len(lib.pa_copy_blocks.argtypes) == 10
