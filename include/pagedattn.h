@@ -24,8 +24,10 @@
  *   - All tensors are dense, row-major, in device memory, 16-byte aligned,
  *     and owned by the caller.  The library never allocates, frees or
  *     synchronises; it keeps no state between calls except each host
- *     thread's last error message (the decode's arrival counters are the
- *     caller's, left at zero by every call).
+ *     thread's last error message, the PAGEDATTN_* options it read from the
+ *     environment, and the static device buffer of pa_decode_step_noalloc
+ *     (the other calls' arrival counters are the caller's, left at zero by
+ *     every call).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     runs asynchronously; results are visible after the caller synchronises.
  *   - Arguments are checked before anything is launched.  On failure the call
@@ -64,10 +66,16 @@ typedef enum pa_dtype {
 /* Library version, major * 10000 + minor * 100 + patch. */
 int32_t pa_version(void);
 
-/* Static text for a status code; never NULL. */
+/*
+ * Static text for a status code; never NULL.  (LLAISYS README, intro and
+ * implemented-features list: a C++ backend behind a C API called from
+ * Python -- errors cross that interface as status codes and text, never as
+ * C++ exceptions.)
+ */
 const char* pa_status_string(int32_t status);
 
-/* Detail of the last failed call made by this host thread ("" if none). */
+/* Detail of the last failed call made by this host thread ("" if none);
+ * same source as pa_status_string. */
 const char* pa_last_error_message(void);
 
 /*
@@ -171,12 +179,22 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pair
 
 /*
  * The partition size (tokens) pa_paged_attention_decode will use for these
- * sizes: `requested` itself if it is a positive multiple of block_size no
- * larger than 128 * block_size; for `requested` 0 the library's own choice
- * (at head_dim 64, 512 tokens for 1 or 2 query heads per kv head and 1024
- * for more; at head_dim 128, 1024 tokens, or 2048 when max_blocks_per_seq *
- * block_size exceeds 4096 -- the fastest measured on MI355X for the decode
- * workloads); -1 if `requested` is invalid.
+ * sizes.  Split-K over a sequence's tokens, each partition's softmax state
+ * merged by a log-sum-exp reduction, is what the long-context workload
+ * states (8 sequences of 32768 tokens, 512-token partitions, cross-partition
+ * log-sum-exp reduce); the LLAISYS README (implemented-features list) has
+ * the last block to arrive finish such a multi-block reduction.
+ *
+ * `requested` itself if it is a positive multiple of block_size no larger
+ * than 128 * block_size.  For `requested` 0 the library's own choice: 0 when
+ * the balanced schedule serves these sizes (num_seqs * num_kv_heads <= 1024
+ * with 1 or 2 query heads per kv head, or with 4 over tables of at most 4096
+ * tokens: equal ranges of the batch's blocks per worker instead of fixed
+ * partitions); otherwise at head_dim 64, 512
+ * tokens for 1 or 2 query heads per kv head and 1024 for more; at head_dim
+ * 128, 1024 tokens, or 2048 when max_blocks_per_seq * block_size exceeds
+ * 4096 -- the fastest measured on MI355X for the decode workloads.  -1 if
+ * `requested` is invalid.
  */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim,
@@ -185,11 +203,14 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
 
 /*
  * Bytes of workspace pa_paged_attention_decode needs for these sizes: the
- * split-K partial results (per sequence, KV head, partition and query head:
- * head_dim floats of unnormalised output plus the running max and sum).
- * 0 when no sequence can span more than one partition, and 0 on invalid
- * sizes.  The workspace needs no initialisation.  Two calls that may run at
- * the same time must not share a workspace.
+ * split-K partial results that the log-sum-exp merge reads (same sources as
+ * pa_decode_partition_size): per piece of a split sequence and query head,
+ * head_dim floats of unnormalised output plus the running max and sum.  With
+ * fixed partitions, one piece per (sequence, KV head, partition); with the
+ * balanced schedule, two per (KV head, worker range).  0 when no sequence
+ * can span more than one piece, and 0 on invalid sizes.  The workspace needs
+ * no initialisation.  Two calls that may run at the same time must not share
+ * a workspace.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim,
@@ -209,7 +230,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *     out[b,h,:] =  sum_t exp(s_t - max s) v_t / sum_t exp(s_t - max s)
  * in float32 arithmetic, rounded once to the storage type (round to nearest
  * even).  L == 0 writes a zero row.  Table entries at or past
- * ceil(L / block_size) are never read.
+ * ceil(L / block_size) may be loaded but are never dereferenced: their
+ * values are not used.
  *
  * Sequences longer than one partition are split into partitions of
  * `partition_size` tokens (0 = library choice, see
@@ -220,7 +242,11 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * atomic arrival counter -- merges them in the same launch; with 16 or more
  * a second kernel, launched on the same stream, merges every split sequence
  * (one long serial merge at the end of the first launch costs more than the
- * launch).  Results do not depend on the order in which partitions finish
+ * launch).  Under the balanced schedule (partition size 0 from
+ * pa_decode_partition_size) each KV head's blocks, sequence after sequence,
+ * are cut into equal ranges, one per worker; a sequence cut by a range
+ * boundary is merged the same way by the last of its pieces to finish.
+ * Results do not depend on the order in which partitions finish
  * (bit-identical reruns).
  *
  *   out            [num_seqs, num_q_heads, head_dim]                   (written)

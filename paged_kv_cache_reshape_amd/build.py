@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 ARCH = "gfx950"
 HIP_SOURCES = ["decode_api.hip", "decode_partition.hip", "decode_mfma.hip", "decode_stream.hip",
-               "prefill_mfma.hip", "kv_write.hip"]
+               "decode_stream_mfma.hip", "prefill_mfma.hip", "kv_write.hip"]
 HOST_SOURCES = ["status.cpp"]
 
 HIPCC_FLAGS = [

@@ -88,21 +88,32 @@ bool deferred_merge(int max_parts) {
 // (PAGEDATTN_MERGE=separate; PAGEDATTN_MERGE=inkernel forces the default).
 bool stream_deferred_merge() { return options().merge == 1; }
 
-// Worker waves in all that the stream schedule aims for: one workgroup of
-// kStreamWaves on each of the 256 compute units.
+// Worker waves in all that the stream schedule aims for.  With 1 or 2 query
+// heads per kv head (vector-ALU worker), one workgroup of kStreamWaves on
+// each of the 256 compute units; with 4 (the matrix-core worker for
+// bfloat16), two per compute unit, whose second workgroup's loads cover the
+// first one's staging and products.  Measured on MI355X, Llama-3.2-shaped
+// batch: 52.3 us at 2048 workers, 78 at 1024, 73 at 2560, 63 at 4096 (the
+// fixed schedule: 62.2).
 constexpr int kStreamWorkersAll = 1024;
+int stream_workers_default(int G) { return G == 4 ? 2048 : kStreamWorkersAll; }
 
-// The stream schedule where it is the library's choice: 1 or 2 query heads
-// per kv head (larger groups keep the matrix-core kernel), and few enough
+// The stream schedule where it is the library's choice: few enough
 // (sequence, kv head) pairs that the fixed schedule would leave compute units
-// without work or unevenly loaded.  PAGEDATTN_SCHEDULE=fixed|stream forces
-// either (stream only where it is built).
-bool stream_eligible(int B, int Hkv, int G, int max_blocks, int requested) {
+// without work or unevenly loaded, with 1 or 2 query heads per kv head, or 4
+// over block tables of at most 4096 tokens (longer sequences split into
+// hundreds of pieces, whose merges cost more than the balance gains: the
+// 32K-token batch took 192-280 us against 168 on the fixed schedule).
+// Groups of 8 or more keep the matrix-core fixed kernel.
+// PAGEDATTN_SCHEDULE=fixed|stream forces either (stream only where it is
+// built).
+bool stream_eligible(int B, int Hkv, int G, int max_blocks, int bs, int requested) {
   if (requested != 0 || !stream_supported(G)) return false;
   if (B > kStreamMaxSeqs || max_blocks > 0xFFFF) return false;
   if (options().schedule == 1) return false;
   if (options().schedule == 2) return true;
-  return G <= 2 && (int64_t)B * Hkv <= kStreamWorkersAll;
+  if ((int64_t)B * Hkv > kStreamWorkersAll) return false;
+  return G <= 2 || (G == 4 && (int64_t)max_blocks * bs <= 4096);
 }
 
 struct Plan {
@@ -132,12 +143,12 @@ bool make_plan(int B, int Hq, int Hkv, int D, int max_blocks, int bs, int reques
   p->stream = false;
   p->stream_workers = 0;
   if (B == 0) return true;
-  if (stream_eligible(B, Hkv, G, max_blocks, requested)) {
+  if (stream_eligible(B, Hkv, G, max_blocks, bs, requested)) {
     // Workers per kv head: the aim, and enough that no range exceeds
     // kStreamMaxRange blocks however the lengths fall; a multiple of the
     // waves of a workgroup.
     const int64_t all = options().stream_workers > 0 ? options().stream_workers
-                                                      : kStreamWorkersAll;
+                                                      : stream_workers_default(G);
     int64_t R = (all + Hkv - 1) / Hkv;
     R = std::max<int64_t>(R, ((int64_t)B * max_blocks + kStreamMaxRange - 1) / kStreamMaxRange);
     R = (R + kStreamWaves - 1) / kStreamWaves * kStreamWaves;
@@ -397,9 +408,11 @@ pa_status decode_impl(void* out, const void* q, bool step, const void* key, cons
   a.new_k = step ? key : nullptr;
   a.new_v = step ? value : nullptr;
 
-  const hipError_t err = plan.stream ? launch_stream(dtype, head_dim, block_size, G, a, s)
-                         : mfma      ? launch_mfma(head_dim, block_size, G, a, s)
-                                     : launch_partition(dtype, head_dim, block_size, G, a, s);
+  const bool stream_mfma = plan.stream && stream_mfma_supported(dtype, G) && !options().valu_only;
+  const hipError_t err = stream_mfma ? launch_stream_mfma(head_dim, block_size, G, a, s)
+                         : plan.stream ? launch_stream(dtype, head_dim, block_size, G, a, s)
+                         : mfma        ? launch_mfma(head_dim, block_size, G, a, s)
+                                       : launch_partition(dtype, head_dim, block_size, G, a, s);
   if (err != hipSuccess) {
     set_error("decode launch failed: %s", hipGetErrorString(err));
     return PA_ERR_HIP;

@@ -54,6 +54,10 @@ __host__ __device__ inline int stream_heads_per_wg(int Hkv) {
 // each kv head's block list, G in {1, 2, 4}; same workspace contract.
 bool stream_supported(int G);
 hipError_t launch_stream(int dtype, int D, int BS, int G, const DecodeArgs& a, hipStream_t s);
+// The balanced schedule's matrix-core worker (decode_stream_mfma.hip):
+// bfloat16, G = 4.  Same ranges, workspace and merge as launch_stream.
+bool stream_mfma_supported(int dtype, int G);
+hipError_t launch_stream_mfma(int D, int BS, int G, const DecodeArgs& a, hipStream_t s);
 // Merge kernel run after a stream launch with deferred_merge set.
 hipError_t launch_stream_merge(int dtype, int D, int BS, int G, const DecodeArgs& a,
                                hipStream_t s);

@@ -203,18 +203,23 @@ def test_partition_size_rule(lib):
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 64) == 1024
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 128) == 2048
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 129) == -1
-    # left to the library: the balanced schedule (reported as 0) for 1 or 2
-    # query heads per kv head and at most 1024 (sequence, kv head) pairs;
-    # otherwise 1024 tokens at head_dim 128 (2048 for tables of more than
-    # 4096 tokens) and 1024 at head_dim 64 for groups of 4 or more
+    # left to the library: the balanced schedule (reported as 0) for at most
+    # 1024 (sequence, kv head) pairs with 1 or 2 query heads per kv head, or
+    # 4 over tables of at most 4096 tokens; otherwise 1024 tokens at
+    # head_dim 128 (2048 for tables of more than 4096 tokens) and 1024 at
+    # head_dim 64 for groups of 4 or more
     assert pa.decode_partition_size(32, 16, 8, 128, 128, 16, 0) == 0
     assert pa.decode_partition_size(64, 16, 8, 64, 256, 16, 0) == 0
     assert pa.decode_partition_size(4, 4, 2, 64, 4, 16, 0) == 0
-    assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 0) == 2048
-    assert pa.decode_partition_size(8, 32, 8, 128, 256, 16, 0) == 1024
+    assert pa.decode_partition_size(64, 32, 8, 64, 256, 16, 0) == 0     # Llama-3.2 shape
+    assert pa.decode_partition_size(8, 32, 8, 128, 256, 16, 0) == 0
+    assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 0) == 2048  # 32K tokens
     assert pa.decode_partition_size(8, 32, 8, 128, 257, 16, 0) == 2048
+    assert pa.decode_partition_size(8, 32, 8, 128, 128, 32, 0) == 0     # 4096 tokens
+    assert pa.decode_partition_size(8, 32, 8, 128, 129, 32, 0) == 2048
     assert pa.decode_partition_size(256, 32, 32, 128, 32, 32, 0) == 1024
-    assert pa.decode_partition_size(64, 32, 8, 64, 256, 16, 0) == 1024
+    assert pa.decode_partition_size(256, 32, 8, 64, 256, 16, 0) == 1024  # 2048 pairs
+    assert pa.decode_partition_size(8, 64, 8, 64, 256, 16, 0) == 1024   # G = 8
     assert pa.decode_partition_size(600, 16, 8, 64, 256, 16, 0) == 512  # 4800 pairs
 
 
@@ -239,6 +244,11 @@ def test_workspace_size_rule(lib):
     rows = Hkv * 128 * 2 * (Hq // Hkv)
     assert pa.decode_workspace_bytes(B, Hq, Hkv, D, mb, bs, 0) == \
         al(rows * D * 4) + al(rows * 2 * 4)
+    # the Llama-3.2 shape (4 query heads per kv head): 2048 workers, 256 per
+    # kv head
+    rows = 8 * 256 * 2 * 4
+    assert pa.decode_workspace_bytes(64, 32, 8, 64, 256, 16, 0) == \
+        al(rows * 64 * 4) + al(rows * 2 * 4)
     # the workers are enough that no range exceeds 128 blocks: 500 sequences
     # of 2048-token tables need 8000 workers per kv head
     rows = 2 * 8000 * 2 * 2

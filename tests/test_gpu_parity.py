@@ -153,6 +153,22 @@ def test_decode_matches_oracle(name):
     G.assert_close(out, ref, w.dtype, name)
 
 
+@pytest.mark.parametrize("name", ["qwen3_0p6b", "llama32_1b", "bf16_d64_bs32_g4",
+                                  "bf16_d128_bs16_g4", "f32_d64_bs16_g1", "bf16_d64_bs16_g2"])
+def test_fixed_schedule_matches_oracle(name, monkeypatch):
+    """The fixed schedule (library partition sizes) on shapes the balanced
+    schedule takes by default: the vector-ALU kernel at 1 or 2 query heads
+    per kv head, the matrix-core kernel at 4."""
+    G.setopt(monkeypatch, "PAGEDATTN_SCHEDULE", "fixed")
+    inp = inputs_for(name)
+    w = inp["workload"]
+    say("write+decode (fixed schedule)", name)
+    d = G.upload(inp)
+    out = G.host_f64(gpu_step(d, 0))
+    ref, _ = oracle_step(inp)
+    G.assert_close(out, ref, w.dtype, name)
+
+
 @pytest.mark.parametrize("name", ["mqa_large", "bf16_d64_bs32_g8", "bf16_d128_bs16_g16",
                                   "llama32_1b", "bf16_d64_bs32_g4", "bf16_d128_bs16_g4"])
 def test_vector_alu_kernel_matches_oracle(name, monkeypatch):
@@ -642,26 +658,42 @@ def test_stream_many_short_sequences(monkeypatch):
     check_stream(inp, "stream many short")
 
 
-def test_stream_library_choice_on_qwen3_shape():
-    """The library's own choice for the Qwen3-shaped batch is the balanced
-    schedule (reported as partition size 0), and its result is the oracle's."""
-    w = synth.WORKLOADS["qwen3_0p6b"]
+@pytest.mark.parametrize("name", ["qwen3_0p6b", "llama32_1b"])
+def test_stream_library_choice(name):
+    """The library's own choice for the Qwen3- and Llama-3.2-shaped batches is
+    the balanced schedule (reported as partition size 0; the vector-ALU and
+    the matrix-core worker), and its result is the oracle's."""
+    w = synth.WORKLOADS[name]
     assert pa.decode_partition_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                     w.max_blocks_per_seq, w.block_size, 0) == 0
-    say("stream qwen3 library choice")
-    check_stream(inputs_for("qwen3_0p6b"), "stream qwen3")
+    say("stream library choice", name)
+    check_stream(inputs_for(name), f"stream {name}")
 
 
-def test_stream_bad_table_entries(monkeypatch):
-    """Block ids outside the pool on the balanced schedule: those sequences'
-    rows are NaN, nothing is dereferenced, every other row keeps its bits
-    (the lengths, hence the ranges, are unchanged); a length past the table
-    gives NaN rows too."""
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bs", [16, 32])
+def test_stream_vector_worker_at_four_heads(D, bs, monkeypatch):
+    """The vector-ALU worker on bfloat16 with 4 query heads per kv head (the
+    matrix-core worker's shapes), forced."""
     G.setopt(monkeypatch, "PAGEDATTN_SCHEDULE", "stream")
-    inp = inputs_for("qwen3_0p6b")
+    G.setopt(monkeypatch, "PAGEDATTN_DECODE_KERNEL", "valu")
+    G.setopt(monkeypatch, "PAGEDATTN_STREAM_WORKERS", 64)
+    inp = stream_case("bf16", D, bs, 4, seed=5)
+    say("stream vector worker G=4", inp["workload"].name)
+    check_stream(inp, f"stream valu {inp['workload'].name}")
+
+
+@pytest.mark.parametrize("name", ["qwen3_0p6b", "llama32_1b"])
+def test_stream_bad_table_entries(name, monkeypatch):
+    """Block ids outside the pool on the balanced schedule (both workers):
+    those sequences' rows are NaN, nothing is dereferenced, every other row
+    keeps its bits (the lengths, hence the ranges, are unchanged); a length
+    past the table gives NaN rows too."""
+    G.setopt(monkeypatch, "PAGEDATTN_SCHEDULE", "stream")
+    inp = inputs_for(name)
     w = inp["workload"]
     B, bs = w.num_seqs, w.block_size
-    say("stream bad table entries")
+    say("stream bad table entries", name)
     d = G.upload(inp)
     base = G.host_storage(gpu_step(d))
     t = inp["block_tables"].copy()
