@@ -26,7 +26,10 @@ the step's algorithmic bytes over the HBM bytes the counters measured on the
 step's launches (a ``--step-only`` run, on the current kernel sources).  ``prior_art`` times the
 pages' earlier design on the same GPU (gather the pages into dense tensors,
 then ordinary attention, in PyTorch).  ``cpu_baseline`` times the float64 CPU
-oracle on a bounded sample of the same batch, and again on one thread.
+oracle on a bounded sample of the same batch, spread over the host's cores
+and again on one thread.  ``read_ceiling`` times kernels that only read the
+decode's K/V bytes, in three access patterns (read_ceiling.hip): the floor
+under any decode that reads the cache that way.
 """
 from __future__ import annotations
 
@@ -50,8 +53,17 @@ METRIC = "decode-attention KV GB/s and % of HBM peak; µs/step at B=32 Qwen3-0.6
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_reshape_amd", "csrc", f)
-               for f in ("decode_partition.hip", "decode_mfma.hip", "attn_common.hpp",
-                         "mfma_attn.hpp", "common.hpp", "decode_launch.hpp", "decode_api.hip")]
+               for f in ("decode_partition.hip", "decode_mfma.hip", "decode_stream.hip",
+                         "decode_stream_mfma.hip",
+                         "attn_common.hpp", "mfma_attn.hpp", "stream_sched.hpp", "common.hpp",
+                         "decode_launch.hpp", "decode_api.hip", "options.hpp")]
+# Worker processes the CPU baseline spreads the oracle over: the host's cores,
+# at most 16 (one GPU's share of a shared host).
+CPU_POOL_MAX = 16
+# A copy of known size made in counter runs (--step-only): rocprofv3's
+# FETCH_SIZE / WRITE_SIZE of the decode kernel are scaled by what they read
+# for this copy.
+CALIBRATION_BYTES = 256 << 20
 
 
 def algorithmic_bytes(inp: dict) -> dict:
@@ -94,11 +106,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def decode_kernel_name(w) -> str:
-    """The decode kernel the library runs for this workload: the matrix-core
-    kernel for bfloat16 with 4, 8, 16 or 32 query heads per kv head (4 only
-    over block tables of at most 4096 tokens), the vector-ALU kernel
-    otherwise."""
+def decode_kernel_name(w, partition_size: int | None = None) -> str:
+    """The decode kernel the library runs for this workload: the balanced
+    schedule's kernel when the library reports partition size 0 (its
+    matrix-core worker for bfloat16 with 4 query heads per kv head), else the
+    matrix-core kernel for bfloat16 with 4, 8, 16 or 32 query heads per kv
+    head (4 only over block tables of at most 4096 tokens), the vector-ALU
+    kernel otherwise."""
+    if partition_size == 0:
+        g = w.num_q_heads // w.num_kv_heads
+        return ("decode_stream_mfma_kernel" if w.dtype == "bf16" and g == 4
+                else "decode_stream_kernel")
     g = w.num_q_heads // w.num_kv_heads
     long_table = w.max_blocks_per_seq * w.block_size > 4096
     mfma = w.dtype == "bf16" and (g in (8, 16, 32) or (g == 4 and not long_table))
@@ -130,6 +148,84 @@ def gather_then_attention(q, k_cache, v_cache, block_tables, context_lens, scale
     p = torch.softmax(s, dim=-1)
     out = torch.matmul(p, vf).reshape(B, hq, d)
     return out.to(q.dtype), (k, v)
+
+
+def gather_then_sdpa(q, k_cache, v_cache, block_tables, context_lens, scale):
+    """The same prior art with PyTorch's fused attention: gather the pages to
+    dense padded tensors, then ``scaled_dot_product_attention`` with a
+    length mask and the query heads grouped over the kv heads (barellm
+    README, feature list: pages gathered into dense tensors before PyTorch
+    SDPA).  Attention runs in float32 (whichever backend PyTorch picks for a
+    masked float32 call).  Returns out [B, Hq, D] in q's dtype."""
+    import torch
+    import torch.nn.functional as F
+    B, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    idx = block_tables.clamp(min=0).long()
+    L = idx.shape[1] * bs
+    k = k_cache[idx].reshape(B, L, hkv, d).transpose(1, 2).float()   # [B, Hkv, L, D]
+    v = v_cache[idx].reshape(B, L, hkv, d).transpose(1, 2).float()
+    live = torch.arange(L, device=q.device)[None, :] < context_lens[:, None].long()
+    out = F.scaled_dot_product_attention(q.float().reshape(B, hq, 1, d), k, v,
+                                         attn_mask=live[:, None, None, :], scale=scale,
+                                         enable_gqa=hq != hkv)
+    return out.reshape(B, hq, d).to(q.dtype)
+
+
+def read_ceilings(torch, w, inp, kcs, vcs, tables, lens, stream, n: int):
+    """Mean µs per launch of the pure-read kernels of ``read_ceiling.hip``
+    (same bytes as the decode's K/V reads, no arithmetic) over n launches
+    cycling the pool copies, HIP events on `stream`: the floor each access
+    pattern puts under a decode.  None where they are not built for the
+    workload (bfloat16 caches only) or the library is missing."""
+    import ctypes
+    path = os.path.join(ROOT, "libreadceiling.so")
+    if w.dtype != "bf16" or not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    f = lib.rc_read_ceiling
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_longlong, ctypes.c_longlong, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    ctx = inp["context_lens"].astype(np.int64)
+    mb = tables.shape[1]
+    blocks = int(np.minimum(-(-ctx // w.block_size), mb).sum())
+    blk_bytes = w.block_size * w.num_kv_heads * w.head_dim * w.elt_bytes
+    nbytes = 2 * blocks * blk_bytes
+    sink = torch.zeros(2048, dtype=torch.int32, device=tables.device)
+    R = len(kcs)
+
+    def launch(mode, i):
+        st = f(mode, kcs[i % R].data_ptr(), vcs[i % R].data_ptr(), tables.data_ptr(),
+               lens.data_ptr(), w.num_seqs, mb, w.num_kv_heads, w.head_dim, w.block_size,
+               nbytes, blocks, sink.data_ptr(), stream.cuda_stream)
+        if st not in (0, -1):
+            raise RuntimeError(f"rc_read_ceiling mode {mode}: HIP error {st}")
+        return st == 0
+
+    out = {"kind": "pure-read kernels (read_ceiling.hip): the decode's K/V bytes, no "
+                   "arithmetic, 256 workgroups",
+           "bytes": nbytes}
+    for mode, name in ((0, "contiguous"), (1, "head_rows"), (2, "token_rows")):
+        if not launch(mode, 0):  # ranges longer than the kernel is built for
+            out[name + "_us"] = None
+            continue
+        for i in range(1, 5):
+            launch(mode, i)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            launch(mode, i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        out[name + "_us"] = round(us, 3)
+        out[name + "_gbs"] = round(nbytes / us / 1e3, 1)
+    return out
 
 
 def _one_thread():
@@ -170,22 +266,82 @@ def _oracle_decode_sample(inp: dict, budget_s: float):
     return done_bytes, seqs_done, time.perf_counter() - t0, time.process_time() - c0
 
 
+_POOL_STATE: dict = {}
+
+
+def _pool_worker(args):
+    """One worker of the spread oracle: decode sequences wid, wid + P, ... of
+    the batch (cycling) until budget_s has passed, on one thread, over the KV
+    caches the parent wrote before forking."""
+    import oracle
+    wid, nproc, budget_s = args
+    inp, k, v = _POOL_STATE["inp"], _POOL_STATE["k"], _POOL_STATE["v"]
+    w = inp["workload"]
+    B = w.num_seqs
+    done, seqs, b = 0, 0, wid
+    t0 = time.perf_counter()
+    with _one_thread():
+        while True:
+            sel = [b % B]
+            oracle.decode(inp["q"][sel], k, v, inp["block_tables"][sel],
+                          inp["context_lens"][sel], inp["scale"], w.dtype)
+            c = int(inp["context_lens"][b % B])
+            done += (c * 2 * w.num_kv_heads * w.head_dim * w.elt_bytes
+                     + 2 * w.num_q_heads * w.head_dim * w.elt_bytes)
+            seqs += 1
+            b += nproc
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    return done, seqs
+
+
+def _oracle_pool_sample(inp: dict, budget_s: float, nproc: int):
+    """The oracle's KV write, then its decode spread over nproc forked worker
+    processes for budget_s.  Returns (KV bytes, sequences, wall s)."""
+    import multiprocessing as mp
+
+    import oracle
+    k, v = oracle.reshape_and_cache(inp["key"], inp["value"], inp["k_cache"],
+                                    inp["v_cache"], inp["slot_mapping"])
+    _POOL_STATE.update(inp=inp, k=k, v=v)
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(nproc) as pool:
+        res = pool.map(_pool_worker, [(i, nproc, budget_s) for i in range(nproc)])
+    dt = time.perf_counter() - t0
+    _POOL_STATE.clear()
+    return sum(r[0] for r in res), sum(r[1] for r in res), dt
+
+
 def cpu_baseline(inp: dict, budget_s: float) -> dict:
-    """Time the float64 oracle's write + decode on a bounded sample, with the
-    host's thread pools as they are and again held to one thread.  `cores` is
-    the number of threads the run kept busy (CPU time over wall time): the
-    oracle's einsum contractions run on one thread either way."""
-    nb, ns, dt, cpu = _oracle_decode_sample(inp, budget_s)
+    """Time the float64 oracle's write + decode on a bounded sample of the
+    batch: spread over the host's cores (one worker process each, at most
+    CPU_POOL_MAX, every worker on one thread: the headline figure), and on one
+    thread alone.  `cores` is the number of worker processes used,
+    `host_cores` the cores this process may run on."""
+    host = len(os.sched_getaffinity(0))
+    nproc = max(1, min(host, CPU_POOL_MAX))
+    nb, ns, dt = _oracle_pool_sample(inp, budget_s, nproc)
     with _one_thread():
         nb1, ns1, dt1, _ = _oracle_decode_sample(inp, budget_s / 3)
     return {"value": round(nb / dt / 1e9, 4), "unit": "GB/s",
-            "cores": _threads_used(cpu, dt), "kind": "oracle",
+            "cores": nproc, "host_cores": host, "kind": "oracle",
             "sample": (f"float64 numpy oracle: one full-pool KV write, then decode of "
-                       f"{ns} sequences of this batch in order "
-                       f"({dt:.1f} s, {nb / 1e6:.1f} MB of KV rows)"),
+                       f"{ns} sequences of this batch (cycling) over {nproc} worker "
+                       f"processes of one thread each ({dt:.1f} s wall, "
+                       f"{nb / 1e6:.1f} MB of KV rows)"),
             "one_thread": {"value": round(nb1 / dt1 / 1e9, 4), "unit": "GB/s",
-                           "sample": f"same, {ns1} sequences with the thread pools held "
-                                     f"to one thread ({dt1:.1f} s)"}}
+                           "sample": f"same on one thread: {ns1} sequences in order "
+                                     f"({dt1:.1f} s)"}}
+
+
+def cpu_baseline_child(workload: str, budget_s: float) -> dict:
+    """cpu_baseline in a child process started before this process touches
+    the GPU (its worker pool forks from a process that never did)."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-only",
+                        "--workload", workload, "--cpu-seconds", str(budget_s)],
+                       capture_output=True, text=True, check=True)
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
@@ -244,7 +400,7 @@ def prefill_cpu_baseline(inp: dict, budget_s: float) -> dict:
                                      f"pools held to one thread ({dt1:.1f} s)"}}
 
 
-def run_prefill(args, torch, pa) -> int:
+def run_prefill(args, torch, pa, cpu_base) -> int:
     """Prefill step: write every new token's K/V rows, then causal prefill
     attention over the paged cache.  value = attention TFLOP/s of the step."""
     w = synth.PREFILL_WORKLOADS[args.workload]
@@ -337,8 +493,8 @@ def run_prefill(args, torch, pa) -> int:
             "flops_per_launch": flops,
         },
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = prefill_cpu_baseline(inp, args.cpu_seconds)
+    if cpu_base is not None:
+        res["cpu_baseline"] = cpu_base
     print(json.dumps(res), flush=True)
     return 0
 
@@ -360,6 +516,8 @@ def main() -> int:
                     help="skip timing the step replayed from a HIP graph")
     ap.add_argument("--no-prior-art", action="store_true",
                     help="skip timing the gather-then-attention PyTorch baseline")
+    ap.add_argument("--cpu-baseline-only", action="store_true",
+                    help="print the CPU baseline of the workload as JSON and exit (no GPU)")
     ap.add_argument("--step-only", action="store_true",
                     help="time the steps only (no separate decode, write or graph timing), "
                          "so that every decode-kernel launch is a fused step: for counter runs")
@@ -370,6 +528,20 @@ def main() -> int:
               "(no sharding, no collectives); run with --gpus 1.", file=sys.stderr)
         return 2
 
+    if args.cpu_baseline_only:
+        if args.workload in synth.PREFILL_WORKLOADS:
+            base = prefill_cpu_baseline(synth.make_prefill_inputs(
+                synth.PREFILL_WORKLOADS[args.workload]), args.cpu_seconds)
+        else:
+            base = cpu_baseline(synth.make_inputs(synth.WORKLOADS[args.workload]),
+                                args.cpu_seconds)
+        print(json.dumps(base), flush=True)
+        return 0
+    # The CPU baseline runs first, in a child process, before anything here
+    # touches the GPU.
+    cpu_base = None if args.no_cpu_baseline else cpu_baseline_child(args.workload,
+                                                                    args.cpu_seconds)
+
     import torch
     import paged_kv_cache_reshape_amd as pa
     if not os.path.exists(pa.LIB_PATH):
@@ -377,7 +549,7 @@ def main() -> int:
         _b.build()
     pa.load_library()
     if args.workload in synth.PREFILL_WORKLOADS:
-        return run_prefill(args, torch, pa)
+        return run_prefill(args, torch, pa, cpu_base)
 
     w = synth.WORKLOADS[args.workload]
     ps = w.partition_size if args.partition_size < 0 else args.partition_size
@@ -443,6 +615,11 @@ def main() -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    if args.step_only:
+        cal = torch.ones(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
+        cal.clone()
+        torch.cuda.synchronize()
+        del cal
     for i in range(args.warmup):
         step(i)
     # The timed region: K whole steps.
@@ -497,14 +674,25 @@ def main() -> int:
             gather_then_attention(q, kcs[i % R], vcs[i % R], tables, lens, scale)
         pa_ms = timed(lambda i: gather_then_attention(q, kcs[i % R], vcs[i % R], tables,
                                                       lens, scale), n_pa, 0)
+        for i in range(3):
+            gather_then_sdpa(q, kcs[i % R], vcs[i % R], tables, lens, scale)
+        sd_ms = timed(lambda i: gather_then_sdpa(q, kcs[i % R], vcs[i % R], tables, lens,
+                                                 scale), n_pa, 0)
         idx = tables.clamp(min=0).long()
         ga_ms = timed(lambda i: (kcs[i % R][idx], vcs[i % R][idx]), n_pa, 0)
         prior = {
-            "kind": "PyTorch: gather pages to dense padded bf16, masked attention in fp32",
+            "kind": "PyTorch: gather pages to dense padded bf16, then attention in fp32",
             "us_per_decode": round(pa_ms * 1e3, 3),
+            "matmul_softmax_us": round(pa_ms * 1e3, 3),
+            "sdpa_us": round(sd_ms * 1e3, 3),
             "dense_gather_us": round(ga_ms * 1e3, 3),
             "decode_speedup": round(pa_ms / (k_mean_s * 1e3), 2),
+            "decode_speedup_vs_sdpa": round(sd_ms / (k_mean_s * 1e3), 2),
         }
+
+    ceilings = None
+    if not args.step_only:
+        ceilings = read_ceilings(torch, w, inp, kcs, vcs, tables, lens, stream, args.steps)
 
     achieved = nbytes["step"] / (ms_step / 1e3) / 1e9
     traffic = None
@@ -558,14 +746,16 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": decode_kernel_name(w) + " (KV write fused)",
+            "kernel": decode_kernel_name(w, part) + " (KV write fused)",
             "bytes_per_launch": nbytes["step"],
         },
     }
+    if ceilings is not None:
+        res["read_ceiling"] = ceilings
     if prior is not None:
         res["prior_art"] = prior
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    if cpu_base is not None:
+        res["cpu_baseline"] = cpu_base
     print(json.dumps(res), flush=True)
     return 0
 

@@ -93,6 +93,26 @@ def build(verbose: bool = False, jobs: int = 4, defines=(), out: str | None = No
     return lib_path
 
 
+# The benchmark's read-ceiling kernels (pure reads of the decode's access
+# patterns), a library of their own beside bench.py: measurement, not part
+# of libpagedattn.
+CEILING_SRC = os.path.join(ROOT, "read_ceiling.hip")
+CEILING_LIB = os.path.join(ROOT, "libreadceiling.so")
+
+
+def build_read_ceiling(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    obj = os.path.join(BUILD_DIR, "read_ceiling.hip.o")
+    _run([_hipcc(), "-x", "hip", *HIPCC_FLAGS, "-c", CEILING_SRC, "-o", obj], verbose)
+    tlib = torch_lib_dir()
+    tmp = CEILING_LIB + ".tmp"
+    _run(["g++", "-shared", "-o", tmp, obj, os.path.join(tlib, "libamdhip64.so"),
+          f"-Wl,-rpath,{tlib}", "-Wl,--no-undefined"], verbose)
+    os.replace(tmp, CEILING_LIB)
+    return CEILING_LIB
+
+
 if __name__ == "__main__":
     path = build(verbose="-v" in sys.argv)
     print(path)
+    print(build_read_ceiling(verbose="-v" in sys.argv))

@@ -2,13 +2,13 @@
 
 Commands (run on the CSV files a GPU run wrote):
 
-  python -m paged_kv_cache_reshape_amd.profiling trace KERNEL_STATS_CSV OUT_MD \\
+  python profiling.py trace KERNEL_STATS_CSV OUT_MD \\
       --command "<the rocprofv3 command that produced it>"
 
-  python -m paged_kv_cache_reshape_amd.profiling traffic FETCH_CSV WRITE_CSV \\
+  python profiling.py traffic FETCH_CSV WRITE_CSV \\
       --workload qwen3_0p6b --partition-size 1024 --command "<...>"
 
-  python -m paged_kv_cache_reshape_amd.profiling counters OUT_MD --kernel NAME \\
+  python profiling.py counters OUT_MD --kernel NAME \\
       --command "<...>" COUNTER_CSV [COUNTER_CSV ...]
 
 ``traffic`` scales the per-dispatch FETCH_SIZE and WRITE_SIZE of the decode
@@ -26,14 +26,17 @@ import json
 import os
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
 def _kernel_key(name: str) -> str:
-    if "decode_partition_kernel" in name or "decode_mfma_kernel" in name:
+    if ("decode_partition_kernel" in name or "decode_mfma_kernel" in name
+            or "decode_stream_kernel" in name or "decode_stream_mfma_kernel" in name):
         return "decode"
+    if "merge_partitions_kernel" in name or "stream_merge_kernel" in name:
+        return "merge"
     if "kv_write_kernel" in name:
         return "kv_write"
     if "copyBuffer" in name:
@@ -61,7 +64,8 @@ def _per_dispatch(counter_csv: str, counter: str) -> dict:
             continue
         k = _kernel_key(r["Kernel_Name"])
         if k == "copy":
-            k = f"copy grid={r['Grid_Size']}"
+            # Each copy on its own: copies of different sizes share a grid.
+            k = f"copy dispatch {r.get('Dispatch_Id', len(grids))}"
             grids[k] = int(r["Grid_Size"])
         agg[k].append(float(r["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in agg.items()}
@@ -80,18 +84,36 @@ def traffic_record(fetch_csv: str, write_csv: str, workload: str, partition_size
                      w.head_dim * w.elt_bytes)
     fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
     write = _per_dispatch(write_csv, "WRITE_SIZE")
-    # The biggest copy kernel clones one K cache: k_cache_bytes read and written.
-    copy_key = max((k for k in fetch if k.startswith("copy")), key=lambda k: fetch[k])
-    fetch_factor = k_cache_bytes / 1024.0 / fetch[copy_key]
-    write_factor = k_cache_bytes / 1024.0 / write[copy_key]
-    # WRITE_SIZE reads a clone's bytes exactly; far from that, the run made no
-    # clone (a pool too large to replicate keeps one copy) and the counters
-    # have nothing of known size to be scaled by.
-    if not 0.9 <= write_factor <= 1.1:
-        raise ValueError(f"the largest copy kernel wrote {write[copy_key]:.1f} KiB, not one "
-                         f"K cache ({k_cache_bytes / 1024.0:.1f} KiB): no clone to scale by")
+    # Copies of known size in the run: the calibration clone `bench.py
+    # --step-only` makes (bench.CALIBRATION_BYTES) and the clones of one K
+    # cache that replicate the pool.  WRITE_SIZE reads a clone's bytes almost
+    # exactly, which tells the copies apart; the largest one found fixes the
+    # scale of each counter.
+    # The two runs make the same dispatches in the same order, so a copy's
+    # dispatch id names it in both.
+    known = {}
+    for k in fetch:
+        if not k.startswith("copy") or k not in write or write[k] <= 0:
+            continue
+        for size in (bench.CALIBRATION_BYTES, k_cache_bytes):
+            if 0.9 <= size / 1024.0 / write[k] <= 1.1:
+                known.setdefault(size, []).append(k)
+    if not known:
+        raise ValueError("no copy kernel wrote a known size (the calibration clone of "
+                         f"{bench.CALIBRATION_BYTES} B or one K cache of {k_cache_bytes} B): "
+                         "no clone to scale by")
+    copy_bytes = max(known)
+    keys = known[copy_bytes]
+    copy_fetch = sum(fetch[k] for k in keys) / len(keys)
+    copy_write = sum(write[k] for k in keys) / len(keys)
+    fetch_factor = copy_bytes / 1024.0 / copy_fetch
+    write_factor = copy_bytes / 1024.0 / copy_write
     read_b = fetch["decode"] * fetch_factor * 1024.0
     write_b = write["decode"] * write_factor * 1024.0
+    # A separate merge kernel (a launch of its own after the decode when a
+    # sequence has many partitions) is reported beside the decode kernel.
+    merge_b = ((fetch.get("merge", 0.0) * fetch_factor + write.get("merge", 0.0) * write_factor)
+               * 1024.0)
     # Counters of a `bench.py --step-only` run see only the fused step's
     # launches (decode with the KV write in it): their algorithmic bytes.
     inp_bytes = bench.algorithmic_bytes(synth.make_inputs(w))["step" if fused_step else "decode"]
@@ -99,14 +121,15 @@ def traffic_record(fetch_csv: str, write_csv: str, workload: str, partition_size
     rec = {
         "workload": workload,
         "partition_size": partition_size,
-        "kernel": bench.decode_kernel_name(w),
+        "kernel": bench.decode_kernel_name(w, partition_size),
         "launch": "fused step" if fused_step else "decode",
         "command": command,
         "fetch_size_kib_per_dispatch": round(fetch["decode"], 2),
         "write_size_kib_per_dispatch": round(write["decode"], 2),
-        "copy_kernel_bytes": k_cache_bytes,
-        "copy_fetch_size_kib": round(fetch[copy_key], 2),
-        "copy_write_size_kib": round(write[copy_key], 2),
+        "copy_kernel_bytes": copy_bytes,
+        "copy_fetch_size_kib": round(copy_fetch, 2),
+        "copy_write_size_kib": round(copy_write, 2),
+        "copy_dispatches": len(keys),
         "fetch_scale": round(fetch_factor, 5),
         "write_scale": round(write_factor, 5),
         "hbm_read_bytes_per_launch": int(read_b),
@@ -114,6 +137,7 @@ def traffic_record(fetch_csv: str, write_csv: str, workload: str, partition_size
         "hbm_bytes_per_launch": int(read_b + write_b),
         "algorithmic_bytes_per_launch": inp_bytes,
         "traffic_over_algorithmic": round((read_b + write_b) / inp_bytes, 4),
+        "merge_kernel_bytes_per_launch": int(merge_b) if "merge" in fetch else None,
         "kernel_source_sha256": bench.kernel_source_hash(),
     }
     json.dump(rec, open(out_json, "w"), indent=1)
@@ -124,12 +148,15 @@ def traffic_record(fetch_csv: str, write_csv: str, workload: str, partition_size
         f"{'launches of the fused step (the KV write inside the decode)' if fused_step else 'decode launches'}.\n\n"
         "Commands (one counter per run):\n\n```\n" + command + "\n```\n\n"
         "| | FETCH_SIZE (KiB/dispatch) | WRITE_SIZE (KiB/dispatch) |\n|---|---|---|\n"
-        f"| copy kernel, {k_cache_bytes} B known | {fetch[copy_key]:.1f} | {write[copy_key]:.1f} |\n"
+        f"| copy kernel, {copy_bytes} B known ({len(keys)} dispatches) | {copy_fetch:.1f} | "
+        f"{copy_write:.1f} |\n"
         f"| scale (known / counter) | {fetch_factor:.5f} | {write_factor:.5f} |\n"
         f"| decode kernel | {fetch['decode']:.1f} | {write['decode']:.1f} |\n\n"
         f"Decode HBM bytes per launch: read {read_b / 1e6:.2f} MB + written "
         f"{write_b / 1e6:.3f} MB = {(read_b + write_b) / 1e6:.2f} MB; algorithmic "
-        f"{inp_bytes / 1e6:.2f} MB (ratio {(read_b + write_b) / inp_bytes:.4f}).\n")
+        f"{inp_bytes / 1e6:.2f} MB (ratio {(read_b + write_b) / inp_bytes:.4f}).\n"
+        + (f"\nSeparate merge kernel (its own launch after each decode): "
+           f"{merge_b / 1e6:.3f} MB per launch.\n" if "merge" in fetch else ""))
     return rec
 
 

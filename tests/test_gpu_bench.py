@@ -37,3 +37,4 @@ def test_bench_prints_one_json_line_with_the_contract_fields():
     assert abs(rl["achieved"] - d["value"]) <= 1e-3 * d["value"]
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    assert cb["host_cores"] >= cb["cores"] and cb["one_thread"]["value"] > 0

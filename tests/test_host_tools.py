@@ -12,7 +12,7 @@ import pytest
 
 import bench
 import synth
-from paged_kv_cache_reshape_amd import profiling
+import profiling
 
 
 def test_algorithmic_bytes_of_the_tiny_batch():
@@ -88,6 +88,30 @@ def test_traffic_record_needs_a_clone_of_known_size(tmp_path, monkeypatch):
     with pytest.raises(ValueError, match="no clone"):
         profiling.traffic_record(str(fetch), str(write), wl, 512, "the commands", True)
     assert not os.path.exists(tmp_path / f"traffic_{wl}.json")
+
+
+def test_traffic_record_takes_the_calibration_copy(tmp_path, monkeypatch):
+    """A pool too large to replicate (one copy, no K clone): the calibration
+    clone of bench.CALIBRATION_BYTES made in the same run scales the
+    counters; a separate merge kernel is reported beside the decode."""
+    wl = "tiny_f32"
+    cal = bench.CALIBRATION_BYTES
+    dec = "void pa::decode_stream_kernel<pa::F32, 64, 16, 2, true>(pa::DecodeArgs)"
+    mrg = "void pa::merge_partitions_kernel<pa::F32, 64, 2>(pa::DecodeArgs)"
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    _counter_csv(fetch, "FETCH_SIZE", [("__amd_rocclr_copyBuffer", cal / 4096, 4096),
+                                       (dec, 100.0, 64), (mrg, 3.0, 8)])
+    _counter_csv(write, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", cal / 1024 * 1.02, 4096),
+                                       (dec, 2.0, 64), (mrg, 1.0, 8)])
+    monkeypatch.setattr(bench, "traffic_file",
+                        lambda workload: str(tmp_path / f"traffic_{workload}.json"))
+    rec = profiling.traffic_record(str(fetch), str(write), wl, 0, "the commands", True)
+    assert rec["copy_kernel_bytes"] == cal
+    assert rec["fetch_scale"] == 4.0
+    assert abs(rec["write_scale"] - 1 / 1.02) < 1e-5
+    assert rec["hbm_read_bytes_per_launch"] == 400 * 1024
+    assert rec["merge_kernel_bytes_per_launch"] == int((3.0 * 4 + 1.0 / 1.02) * 1024)
+    assert rec["kernel"] == "decode_stream_kernel"
 
 
 def test_bench_refuses_more_than_one_gpu():
