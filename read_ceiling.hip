@@ -8,7 +8,7 @@
 // measurements beside the library, never part of it.
 //
 //   mode 0, contiguous: the same byte count read as one contiguous range of
-//           K and one of V (256 workgroups, equal shares).
+//           K and one of V (256 workgroups of 8 waves, equal shares).
 //   mode 1, head rows: the decode's balanced schedule -- each kv head's block
 //           list cut into equal ranges; a 4-wave workgroup reads four
 //           neighbouring kv heads of one range, each wave its head's
@@ -95,17 +95,19 @@ __device__ void range_entries(const Args& a, const int* s_cum, int s, int n, int
   }
 }
 
-__global__ __launch_bounds__(256) void read_contiguous(Args a) {
+// 8 waves, 8 loads of 16 bytes in flight per lane (64 KB per workgroup).
+__global__ __launch_bounds__(512) void read_contiguous(Args a) {
+  constexpr int U = 8, STEP = 512 * 16;
   const long long per = a.flat_bytes / (kWorkgroups / 2);
   const char* base = blockIdx.x < kWorkgroups / 2 ? a.k : a.v;
   const long long lo = per * (blockIdx.x % (kWorkgroups / 2));
   uint32_t acc = 0;
-  for (long long o = lo + threadIdx.x * 16; o < lo + per; o += 4 * 256 * 16) {
-    u32x4 r[4];
+  for (long long o = lo + threadIdx.x * 16; o < lo + per; o += U * STEP) {
+    u32x4 r[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) r[u] = o + u * 4096 < lo + per ? ld(base + o + u * 4096) : u32x4{};
+    for (int u = 0; u < U; ++u) r[u] = o + u * STEP < lo + per ? ld(base + o + u * STEP) : u32x4{};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc += fold(r[u]);
+    for (int u = 0; u < U; ++u) acc += fold(r[u]);
   }
   if (acc == 0x9E3779B9u) a.sink[blockIdx.x] = acc;
 }
@@ -227,7 +229,7 @@ extern "C" int rc_read_ceiling(int mode, const void* k_cache, const void* v_cach
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (mode == 0) {
     a.flat_bytes = kv_bytes / 2 / (kWorkgroups / 2) / 16 * 16 * (kWorkgroups / 2);
-    read_contiguous<<<kWorkgroups, 256, 0, s>>>(a);
+    read_contiguous<<<kWorkgroups, 512, 0, s>>>(a);
   } else if (mode == 1) {
     const int hw = num_kv_heads % 4 == 0 ? 4 : num_kv_heads % 2 == 0 ? 2 : 1;
     const int ngr = num_kv_heads / hw;
