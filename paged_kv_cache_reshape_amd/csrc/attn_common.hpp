@@ -121,6 +121,7 @@ __device__ __forceinline__ float collect(const float* p) {
 // wide accesses instead of one 4-byte transaction per value.
 constexpr int kBufferWord3 = 0x00020000;  // gfx9 raw buffer, 32-bit data format
 constexpr int kSystemCoherent = 17;       // cache-policy operand: sc0 | sc1
+constexpr int kLoadNT = 2;                // cache-policy operand of data read once: nt
 struct CoherentRegion {
   __amdgpu_buffer_rsrc_t r;
   // base must be the same in every lane; accesses are range-checked against
@@ -307,8 +308,9 @@ struct RowAttn {
 // Walk blocks jj = first, first + step, ... < n with the next PF-1 blocks'
 // loads in flight while the current one is consumed.  Written so that the
 // compiler keeps that overlap: the loop body has no branch (a block index at
-// or past n is fetched as block n-1, which is in bounds, and consumed with
-// every row masked), the ring of PF buffers is indexed with constants only
+// or past n is fetched as block n-1, which is in bounds, with `live` false
+// so that the fetch can read nothing, and consumed with every row masked),
+// the ring of PF buffers is indexed with constants only
 // (the loop is unrolled by PF), and a scheduling barrier keeps each prefetch
 // issued ahead of the arithmetic that does not need it.
 template <int NL, int PF = PA_PREFETCH_DEPTH, class Fetch, class Consume>
@@ -319,13 +321,15 @@ __device__ __forceinline__ void stream_blocks(int first, int step, int n, Fetch&
   uint4 kr[PF][NL], vr[PF][NL];
 #pragma unroll
   for (int p = 0; p < PF - 1; ++p) {
-    fetch(clamp(first + p * step), kr[p], vr[p]);
+    const int j = first + p * step;
+    fetch(clamp(j), j < n, kr[p], vr[p]);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads of one block together
   }
   for (int jj = first; jj < n; jj += PF * step) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
-      fetch(clamp(jj + (u + PF - 1) * step), kr[(u + PF - 1) % PF], vr[(u + PF - 1) % PF]);
+      const int jn = jj + (u + PF - 1) * step;
+      fetch(clamp(jn), jn < n, kr[(u + PF - 1) % PF], vr[(u + PF - 1) % PF]);
       __builtin_amdgcn_sched_barrier(0);
       const int j = jj + u * step;
       consume(j, j < n, kr[u], vr[u]);

@@ -81,12 +81,13 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   const uint32_t head_off = (uint32_t)g * D * 2 + 16 * col;
   const char* kbase = static_cast<const char*>(a.k_cache);
   const char* vbase = static_cast<const char*>(a.v_cache);
-  auto fetch = [&](int jb, uint4 (&kr)[NI], uint4 (&vr)[NI]) {
+  auto fetch = [&](int jb, bool live, uint4 (&kr)[NI], uint4 (&vr)[NI]) {
     const size_t boff = (size_t)w.block(jb) * blk_bytes;
+    const uint32_t nrec = live ? blk_bytes : 0u;  // a prefetch past the end reads nothing
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(kbase + boff), 0, blk_bytes, kBufferRsrcWord3);
+        const_cast<char*>(kbase + boff), 0, nrec, kBufferRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(vbase + boff), 0, blk_bytes, kBufferRsrcWord3);
+        const_cast<char*>(vbase + boff), 0, nrec, kBufferRsrcWord3);
     const int pos0 = (w.blk0 + jb) * BS;
     uint32_t off[NI];
 #pragma unroll

@@ -53,14 +53,31 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
   const int ctx = w.ctx, blk0 = w.blk0;
 
   st.reset();
-  const size_t tok_stride = (size_t)Hkv * D;
-  const size_t blk_stride = tok_stride * BS;
-  const int lane_off = row * Hkv * D + col * E;
-  const S* kbase = static_cast<const S*>(a.k_cache) + (size_t)g * D + lane_off;
-  const S* vbase = static_cast<const S*>(a.v_cache) + (size_t)g * D + lane_off;
-  auto fetch = [&](int j, uint4 (&kr)[NI], uint4 (&vr)[NI]) {
-    const size_t off = (size_t)w.block(j) * blk_stride;
-    Row::fetch(kbase + off, vbase + off, tok_stride, kr, vr);
+  // A block's rows through buffer loads over that block: 16 bytes a lane at
+  // d = E col of token t ROWS + row.  The prefetch past a wave's last block
+  // (live false) gets a resource of zero bytes, so it reads nothing instead
+  // of the last block once more.
+  constexpr int ROWS = Sh::ROWS;
+  const uint32_t tok_bytes = (uint32_t)((size_t)Hkv * D * sizeof(S));
+  const uint32_t blk_bytes = tok_bytes * BS;
+  const uint32_t lane_bytes = (uint32_t)(((size_t)row * Hkv * D + (size_t)g * D + col * E) * sizeof(S));
+  const char* kbase = static_cast<const char*>(a.k_cache);
+  const char* vbase = static_cast<const char*>(a.v_cache);
+  auto fetch = [&](int j, bool live, uint4 (&kr)[NI], uint4 (&vr)[NI]) {
+    const size_t off = (size_t)w.block(j) * blk_bytes;
+    const uint32_t n = live ? blk_bytes : 0u;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + off), 0, n, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + off), 0, n, kBufferWord3);
+#pragma unroll
+    for (int t = 0; t < NI; ++t)
+      kr[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rk, lane_bytes + t * ROWS * tok_bytes, 0, kLoadNT));
+#pragma unroll
+    for (int t = 0; t < NI; ++t)
+      vr[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rv, lane_bytes + t * ROWS * tok_bytes, 0, kLoadNT));
   };
   auto consume = [&](int j, bool live, const uint4 (&kr)[NI], const uint4 (&vr)[NI]) {
     st.consume((blk0 + j) * BS + row, ctx, live, a.scale_log2, kr, vr);

@@ -82,9 +82,11 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
   const int row = lane / RL, col = lane % RL;
   const size_t tok_stride = (size_t)Hkv * D;
   const size_t blk_stride = tok_stride * BS;
-  const size_t lane_off = (size_t)row * tok_stride + (size_t)h * D + col * E;
-  const S* kbase = static_cast<const S*>(a.k_cache) + lane_off;
-  const S* vbase = static_cast<const S*>(a.v_cache) + lane_off;
+  const uint32_t tok_bytes = (uint32_t)(tok_stride * sizeof(S));
+  const uint32_t blk_bytes = tok_bytes * BS;
+  const uint32_t lane_bytes = (uint32_t)(((size_t)row * tok_stride + (size_t)h * D + col * E) * sizeof(S));
+  const char* kbase = static_cast<const char*>(a.k_cache);
+  const char* vbase = static_cast<const char*>(a.v_cache);
   const S* qbase = static_cast<const S*>(a.q) + (size_t)h * G * D + col * E;
   const S* nkbase = FUSED ? static_cast<const S*>(a.new_k) + (size_t)h * D + col * E : nullptr;
   const S* nvbase = FUSED ? static_cast<const S*>(a.new_v) + (size_t)h * D + col * E : nullptr;
@@ -92,10 +94,27 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
   struct Slot {
     uint4 k[NI], v[NI], q[G], nk, nv;
   };
-  auto fetch = [&](int i, Slot& sl) {
-    const size_t off = (size_t)w.entry(i) * blk_stride;
+  // Block i's rows through buffer loads over that block (16 bytes a lane at
+  // d = E col of token t ROWS + row).  A prefetch past the range's end
+  // (live false) gets a resource of zero bytes: its loads return zeros and
+  // read nothing, where re-reading the last block would cost a block of HBM
+  // traffic per wave.
+  auto fetch = [&](int i, bool live, Slot& sl) {
+    const size_t off = (size_t)w.entry(i) * blk_stride * sizeof(S);
     const int b = (w.seqblk(i) >> 16) & 0x7FFF;
-    Row::fetch(kbase + off, vbase + off, tok_stride, sl.k, sl.v);
+    const uint32_t n = live ? blk_bytes : 0u;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + off), 0, n, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + off), 0, n, kBufferWord3);
+#pragma unroll
+    for (int t = 0; t < NI; ++t)
+      sl.k[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rk, lane_bytes + t * ROWS * tok_bytes, 0, kLoadNT));
+#pragma unroll
+    for (int t = 0; t < NI; ++t)
+      sl.v[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rv, lane_bytes + t * ROWS * tok_bytes, 0, kLoadNT));
 #pragma unroll
     for (int gh = 0; gh < G; ++gh) sl.q[gh] = load_chunk(qbase + ((size_t)b * Hq + gh) * D);
     if constexpr (FUSED) {
@@ -236,13 +255,14 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
   const auto clampi = [&](int i) { return i < w.n ? i : w.n - 1; };
 #pragma unroll
   for (int p = 0; p < PF - 1; ++p) {
-    fetch(clampi(p), sl[p]);
+    fetch(clampi(p), p < w.n, sl[p]);
     __builtin_amdgcn_sched_barrier(0);
   }
   for (int i0 = 0; i0 < w.n; i0 += PF) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
-      fetch(clampi(i0 + u + PF - 1), sl[(u + PF - 1) % PF]);
+      const int nx = i0 + u + PF - 1;
+      fetch(clampi(nx), nx < w.n, sl[(u + PF - 1) % PF]);
       __builtin_amdgcn_sched_barrier(0);
       if (i0 + u < w.n) consume(i0 + u, sl[u]);
     }

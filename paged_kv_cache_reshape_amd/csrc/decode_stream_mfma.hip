@@ -83,13 +83,16 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_mfma_kernel(D
   struct Slot {
     uint4 k[NI], v[NI], q[HT][DK], nk, nv;
   };
-  auto fetch = [&](int i, Slot& sl) {
+  // A prefetch past the range's end (live false) gets a resource of zero
+  // bytes: its loads return zeros and read nothing.
+  auto fetch = [&](int i, bool live, Slot& sl) {
     const size_t boff = (size_t)w.entry(i) * blk_bytes;
     const int b = (w.seqblk(i) >> 16) & 0x7FFF;
+    const uint32_t nrec = live ? blk_bytes : 0u;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(kbase + boff), 0, blk_bytes, kBufferRsrcWord3);
+        const_cast<char*>(kbase + boff), 0, nrec, kBufferRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(vbase + boff), 0, blk_bytes, kBufferRsrcWord3);
+        const_cast<char*>(vbase + boff), 0, nrec, kBufferRsrcWord3);
 #pragma unroll
     for (int t = 0; t < NI; ++t)
       sl.k[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -244,13 +247,14 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_mfma_kernel(D
   const auto clampi = [&](int i) { return i < w.n ? i : w.n - 1; };
 #pragma unroll
   for (int p = 0; p < PF - 1; ++p) {
-    fetch(clampi(p), sl[p]);
+    fetch(clampi(p), p < w.n, sl[p]);
     __builtin_amdgcn_sched_barrier(0);
   }
   for (int i0 = 0; i0 < w.n; i0 += PF) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
-      fetch(clampi(i0 + u + PF - 1), sl[(u + PF - 1) % PF]);
+      const int nx = i0 + u + PF - 1;
+      fetch(clampi(nx), nx < w.n, sl[(u + PF - 1) % PF]);
       __builtin_amdgcn_sched_barrier(0);
       if (i0 + u < w.n) consume(i0 + u, sl[u]);
     }

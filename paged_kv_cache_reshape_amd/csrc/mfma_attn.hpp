@@ -56,7 +56,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBufferRsrcWord3 = kBufferWord3;
 // Cache-policy operand of a buffer load that reads data once per launch:
 // the non-temporal bit ("nt", bit 1 on gfx950).
-constexpr int kLoadStreaming = 2;
+constexpr int kLoadStreaming = kLoadNT;
 
 template <int D, int BS, int NR>
 struct TileShape {
