@@ -208,7 +208,8 @@ def read_ceilings(torch, w, inp, kcs, vcs, tables, lens, stream, n: int):
     out = {"kind": "pure-read kernels (read_ceiling.hip): the decode's K/V bytes, no "
                    "arithmetic, 256 workgroups",
            "bytes": nbytes}
-    for mode, name in ((0, "contiguous"), (1, "head_rows"), (2, "token_rows")):
+    for mode, name in ((0, "contiguous"), (1, "head_rows"), (2, "token_rows"),
+                       (3, "head_interleaved")):
         if not launch(mode, 0):  # ranges longer than the kernel is built for
             out[name + "_us"] = None
             continue

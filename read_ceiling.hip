@@ -16,6 +16,10 @@
 //   mode 2, token rows: the batch's block list cut into equal ranges, one per
 //           workgroup of 8 waves, which reads whole blocks (every kv head of
 //           every token: one contiguous run per block), two in flight.
+//   mode 3, interleaved head rows: each kv head's block list cut into
+//           256 / num_kv_heads equal ranges, one per 4-wave workgroup, whose
+//           waves take every fourth block of the range (the head's slice of
+//           each token row), two in flight.
 //
 // bfloat16 caches, head_dim 64 or 128, block_size 16 or 32, at most 2048
 // sequences and 128 blocks per range.
@@ -159,6 +163,69 @@ __global__ __launch_bounds__(256) void read_head_rows(Args a, int heads_per_wg) 
   if (acc == 0x9E3779B9u) a.sink[blockIdx.x * 4 + wave] = acc;
 }
 
+// One kv head per 4-wave workgroup, waves interleaving the blocks of one
+// range (wave w takes blocks w, w + 4, ...): NI 16-byte loads per lane cover
+// the head's slice of a block.
+template <int NI>
+__global__ __launch_bounds__(256) void read_head_interleaved(Args a) {
+  __shared__ int s_cum[kMaxSeqs + 1];
+  __shared__ int s_part[4];
+  const int T = prefix_blocks<256>(a, s_cum, s_part);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.x % a.Hkv, r = blockIdx.x / a.Hkv, R = a.ranges;
+  const int s = (int)((long long)r * T / R), n = (int)((long long)(r + 1) * T / R) - s;
+  // This wave's blocks of the range: i = wave + 4 k < n.
+  const int nw = n > wave ? (n - wave + 3) / 4 : 0;
+  int ent[2];
+  {
+    // entries of this wave's blocks k = lane and 64 + lane
+    ent[0] = ent[1] = 0;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int k = 64 * hh + lane;
+      if (k < nw) {
+        const int g = s + wave + 4 * k;
+        int lo = 0, hi = a.B;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_cum[mid] <= g) lo = mid; else hi = mid;
+        }
+        ent[hh] = a.tables[(long long)lo * a.max_blocks + (g - s_cum[lo])];
+      }
+    }
+  }
+  const int RL = a.row_bytes / 16, ROWS = 64 / RL;
+  const long long tok = (long long)a.Hkv * a.row_bytes, blk = tok * a.bs;
+  const long long loff = (long long)(lane / RL) * tok + (long long)h * a.row_bytes + (lane % RL) * 16;
+  auto entry = [&](int i) { return __builtin_amdgcn_readlane(i < 64 ? ent[0] : ent[1], i & 63); };
+  u32x4 kr[2][NI], vr[2][NI];
+  auto fetch = [&](int i, u32x4 (&k)[NI], u32x4 (&v)[NI]) {
+    const long long base = (long long)entry(i) * blk + loff;
+#pragma unroll
+    for (int t = 0; t < NI; ++t) k[t] = ld(a.k + base + t * ROWS * tok);
+#pragma unroll
+    for (int t = 0; t < NI; ++t) v[t] = ld(a.v + base + t * ROWS * tok);
+  };
+  uint32_t acc = 0;
+  if (nw > 0) {
+    fetch(0, kr[0], vr[0]);
+    for (int i = 0; i < nw; i += 2) {
+      fetch(min(i + 1, nw - 1), kr[1], vr[1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < NI; ++t) acc += fold(kr[0][t]) + fold(vr[0][t]);
+      fetch(min(i + 2, nw - 1), kr[0], vr[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < nw) {
+#pragma unroll
+        for (int t = 0; t < NI; ++t) acc += fold(kr[1][t]) + fold(vr[1][t]);
+      }
+    }
+  }
+  if (acc == 0x9E3779B9u) a.sink[blockIdx.x * 4 + wave] = acc;
+}
+
 // CPW 16-byte loads per lane of an 8-wave workgroup cover one whole block.
 template <int CPW>
 __global__ __launch_bounds__(512) void read_token_rows(Args a) {
@@ -253,6 +320,18 @@ extern "C" int rc_read_ceiling(int mode, const void* k_cache, const void* v_cach
       case 2: read_token_rows<2><<<kWorkgroups, 512, 0, s>>>(a); break;
       case 4: read_token_rows<4><<<kWorkgroups, 512, 0, s>>>(a); break;
       case 8: read_token_rows<8><<<kWorkgroups, 512, 0, s>>>(a); break;
+      default: return -1;
+    }
+  } else if (mode == 3) {
+    if (kWorkgroups % num_kv_heads) return -1;
+    a.ranges = kWorkgroups / num_kv_heads;  // ranges per kv head
+    // each wave holds at most 128 of its range's blocks
+    if ((total_blocks + a.ranges - 1) / a.ranges > 4 * kMaxRange) return -1;
+    const int ni = block_size * a.row_bytes / 1024;
+    switch (ni) {
+      case 2: read_head_interleaved<2><<<kWorkgroups, 256, 0, s>>>(a); break;
+      case 4: read_head_interleaved<4><<<kWorkgroups, 256, 0, s>>>(a); break;
+      case 8: read_head_interleaved<8><<<kWorkgroups, 256, 0, s>>>(a); break;
       default: return -1;
     }
   } else {
