@@ -341,19 +341,18 @@ __device__ __forceinline__ void stream_blocks(int first, int step, int n, Fetch&
 // output.  `row_of(p, r)` returns the row index (into ws_ml / 2 and ws_acc /
 // D) of output row r in piece p, so the rows of several kv heads, which lie
 // apart in the workspace, merge in one pass.  Pieces are read in index order
-// through LDS in chunks of 64, so the result does not depend on the order in
-// which they were written.  Used by one whole workgroup; `gh` rows of D values
+// through LDS in chunks of kChunk (s_pm / s_pl hold that many), so the result
+// does not depend on the order in which they were written.  Used by one whole workgroup; `gh` rows of D values
 // each, output at out + out_base (rows consecutive).
 //
 // The partial outputs are read with system-scope loads, which go to memory:
 // every thread first issues the loads of U pieces for all its output
 // elements, then folds them in, so that U * EPT (about kInFlight) loads are
 // in flight per thread instead of one round trip per value.
-template <class DT, int D, int GH, int NT, int kInFlight = 16, class RowFn>
+template <class DT, int D, int GH, int NT, int kInFlight = 16, int kChunk = 64, class RowFn>
 __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int npieces, int gh,
                                              RowFn row_of, size_t out_base,
                                              float (*s_pm)[GH], float (*s_pl)[GH]) {
-  constexpr int kChunk = 64;
   constexpr int EPT = (GH * D + NT - 1) / NT;  // output elements per thread, at most
   constexpr int U = EPT >= kInFlight ? 1 : kInFlight / EPT;  // pieces loaded together
   const int tid = threadIdx.x;
@@ -574,9 +573,12 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
   // most kv heads a workgroup takes, so kRows bounds its output rows.
   constexpr bool kRowFactors = G >= 8;
   constexpr int kRows = HPW * G;
-  static_assert(NW * GW <= 64 * kRows, "combine factors must fit the merge's LDS area");
-  __shared__ float s_pm[64][kRows];
-  __shared__ float s_pl[64][kRows];
+  // The merge in this launch takes fewer than 16 pieces (16 or more go to the
+  // merge kernel), so its LDS area holds 16 pieces' (max, sum) per row.
+  constexpr int kPieces = 16;
+  static_assert(NW * GW <= kPieces * kRows, "combine factors must fit the merge's LDS area");
+  __shared__ float s_pm[kPieces][kRows];
+  __shared__ float s_pl[kPieces][kRows];
   const int rows = hpw * G;
   float* s_fac = &s_pm[0][0];  // [t][r]: t * rows + r
   float* s_rm = &s_pl[0][0];
@@ -689,7 +691,7 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
   // 33.04 -> 32.88 us, Llama-3.2 batch 66.4 -> 66.1 us against 16).
   const auto merge = [&](auto gh) {
     constexpr int GH = decltype(gh)::value;
-    merge_pieces<DT, D, GH, NT, 8>(a, nparts, rows, row_of, out_base,
+    merge_pieces<DT, D, GH, NT, 8, kPieces>(a, nparts, rows, row_of, out_base,
                                 reinterpret_cast<float (*)[GH]>(&s_pm[0][0]),
                                 reinterpret_cast<float (*)[GH]>(&s_pl[0][0]));
   };

@@ -23,6 +23,9 @@
 // block's first token, in range and finite, and are masked), marked
 // non-temporal since each is read once, and stages them in its own LDS tile.
 #include "mfma_attn.hpp"
+#include "mfma_tile32.hpp"
+
+#include <type_traits>
 
 #include "decode_launch.hpp"
 
@@ -39,10 +42,15 @@ constexpr int kGroupPrefetch = 1;
 template <int D, int BS, int G, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   using Sh = TileShape<D, BS, G>;
-  using T = RowTileAttn<D, BS, G>;
+  // 32 query heads over 32-token blocks: one 32-row tile and one 32-key fold
+  // per block on v_mfma_f32_32x32x16_bf16 (mfma_tile32.hpp), half the
+  // instructions of the 16x16x32 form for the same products.
+  constexpr bool kT32 = G == 32 && BS == 32;
+  using T = std::conditional_t<kT32, RowTile32Attn<D>, RowTileAttn<D, BS, G>>;
   constexpr int RL = Sh::RL, ROWS = Sh::ROWS, NI = Sh::NI;
-  constexpr int KPITCH = Sh::KPITCH, VPITCH = Sh::VPITCH;
-  constexpr int KTILE = Sh::KTILE, VTILE = Sh::VTILE;
+  constexpr int KPITCH = kT32 ? Tile32Shape<D>::KPITCH : Sh::KPITCH;
+  constexpr int VPITCH = kT32 ? Tile32Shape<D>::VPITCH : Sh::VPITCH;
+  constexpr int KTILE = BS * KPITCH, VTILE = BS * VPITCH;
   constexpr int NT = NW * 64;
   // LDS: per wave a K and a V tile while streaming; afterwards the same bytes
   // hold the waves' states for the combine.
@@ -115,13 +123,17 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     }
     __builtin_amdgcn_wave_barrier();
     // Every existing row sits at the newest position; masked when not live.
-    int rowpos[T::HT];
-#pragma unroll
-    for (int ht = 0; ht < T::HT; ++ht)
-      rowpos[ht] = live && 16 * ht + (lane & 15) < G ? w.ctx - 1 : -1;
     // Only the sequence's last block holds keys past the newest position.
     const int pos0 = (w.blk0 + jb) * BS;
-    st.consume(kt, vt, pos0, rowpos, !live || pos0 + BS > w.ctx, qs.c, lane);
+    if constexpr (kT32) {
+      st.consume(kt, vt, pos0, live ? w.ctx - 1 : -1, !live || pos0 + BS > w.ctx, qs.c, lane);
+    } else {
+      int rowpos[T::HT];
+#pragma unroll
+      for (int ht = 0; ht < T::HT; ++ht)
+        rowpos[ht] = live && 16 * ht + (lane & 15) < G ? w.ctx - 1 : -1;
+      st.consume(kt, vt, pos0, rowpos, !live || pos0 + BS > w.ctx, qs.c, lane);
+    }
     __builtin_amdgcn_wave_barrier();
   };
   stream_blocks<NI, kGroupPrefetch>(tw, nwt, w.nblk_run, fetch, consume);

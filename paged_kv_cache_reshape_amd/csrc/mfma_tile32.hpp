@@ -1,5 +1,6 @@
 // Matrix-core attention for 32 query rows per wave on 32x32x16 bfloat16
-// tiles (v_mfma_f32_32x32x16_bf16), used by the prefill kernel.
+// tiles (v_mfma_f32_32x32x16_bf16), used by the prefill kernel and by the
+// decode of 32 query heads per kv head over 32-token blocks.
 //
 // On MI355X this instruction sustains about twice the rate per flop of the
 // 16x16x32 form (measured: 2.3 against 1.3 PFLOP/s with independent
@@ -175,6 +176,21 @@ struct RowTile32Attn {
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl[h], b, o[dt], 0, 0, 0);
       }
     }
+  }
+
+  // Write the wave's state to LDS: s_acc[row][d], s_m[row], s_l[row] (row
+  // sums over both halves' tokens), for the 32 rows.
+  __device__ __forceinline__ void to_lds(float (*s_acc)[D], float* s_m, float* s_l,
+                                         int lane) const {
+    const float t = l + lane_xor<32>(l);
+    if (lane < 32) {
+      s_m[lane] = m;
+      s_l[lane] = t;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_acc[row32(lane, r)][32 * dt + (lane & 31)] = o[dt][r];
   }
 
   // Normalised output: store(row, d, value) for every row < 32 and d < D.

@@ -40,6 +40,9 @@ EXTRA = {
                                        ("uniform", 1, 900), num_blocks=200, seed=37),
     "bf16_d128_bs16_g4": synth.Workload("bf16_d128_bs16_g4", 6, 16, 4, 128, 16, "bf16",
                                         ("uniform", 1, 1500), seed=38),
+    # 32 query heads per kv head over 32-token blocks: the 32x32-tile decode.
+    "bf16_d64_bs32_g32": synth.Workload("bf16_d64_bs32_g32", 7, 64, 2, 64, 32, "bf16",
+                                        ("uniform", 1, 1200), seed=39),
 }
 
 
@@ -229,7 +232,7 @@ def test_decode_long_split_k(long_splitk_oracle, ps):
 @pytest.mark.parametrize("merge", ["inkernel", "separate"])
 @pytest.mark.parametrize("name,ps", [("f32_d128_bs32_g4", 64), ("bf16_d128_bs16_g16", 128),
                                      ("bf16_d64_bs16_g2", 256), ("bf16_d64_bs32_g8", 64),
-                                     ("llama32_1b", 512)])
+                                     ("llama32_1b", 512), ("bf16_d64_bs32_g32", 64)])
 def test_merge_paths_match_oracle(name, ps, merge, monkeypatch):
     """Split sequences merged by the last partition workgroup to arrive, or by
     the merge kernel that follows the partition launch."""
@@ -475,7 +478,8 @@ def fused_step(d, partition_size=0):
 
 
 @pytest.mark.parametrize("name,ps", [("qwen3_0p6b", 0), ("qwen3_0p6b", 64), ("tiny_f32", 0),
-                                     ("llama32_1b", 0), ("mqa_large", 0),
+                                     ("llama32_1b", 0), ("mqa_large", 0), ("mqa_large", 256),
+                                     ("bf16_d64_bs32_g32", 96),
                                      ("bf16_d128_bs16_g16", 128), ("bf16_d128_bs16_g16", 32),
                                      ("bf16_d64_bs32_g8", 0), ("f32_d128_bs32_g4", 64)])
 def test_decode_step_equals_write_then_decode(name, ps):
