@@ -188,9 +188,9 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pair
  * `requested` itself if it is a positive multiple of block_size no larger
  * than 128 * block_size.  For `requested` 0 the library's own choice: 0 when
  * the balanced schedule serves these sizes (num_seqs * num_kv_heads <= 1024
- * with 1 or 2 query heads per kv head, or with 4 over tables of at most 4096
- * tokens: equal ranges of the batch's blocks per worker instead of fixed
- * partitions); otherwise at head_dim 64, 512
+ * with 1 or 2 query heads per kv head, or with 4 at head_dim 64 over tables
+ * of at most 4096 tokens: equal ranges of the batch's blocks per worker
+ * instead of fixed partitions); otherwise at head_dim 64, 512
  * tokens for 1 or 2 query heads per kv head and 1024 for more; at head_dim
  * 128, 1024 tokens, or 2048 when max_blocks_per_seq * block_size exceeds
  * 4096 -- the fastest measured on MI355X for the decode workloads.  -1 if

@@ -101,19 +101,25 @@ int stream_workers_default(int G) { return G == 4 ? 2048 : kStreamWorkersAll; }
 // The stream schedule where it is the library's choice: few enough
 // (sequence, kv head) pairs that the fixed schedule would leave compute units
 // without work or unevenly loaded, with 1 or 2 query heads per kv head, or 4
-// over block tables of at most 4096 tokens (longer sequences split into
-// hundreds of pieces, whose merges cost more than the balance gains: the
-// 32K-token batch took 192-280 us against 168 on the fixed schedule).
+// at head_dim 64 over block tables of at most 4096 tokens.  Measured on
+// MI355X with 4 query heads per kv head:
+//   - head_dim 64: 64 sequences of up to 4096 tokens, 49.1 against 59.5 us
+//     (16-token blocks) and 50.8 against 61.9 (32-token blocks);
+//   - head_dim 128, where the matrix-core worker holds one wave per SIMD: 32
+//     sequences of up to 2048 tokens, 51.1 (39.9 at 1024 workers) against
+//     36.3 us on the fixed schedule, so it stays there;
+//   - longer tables split sequences into hundreds of pieces, whose merges cost
+//     more than the balance gains (the 32K-token batch: 192-280 against 168 us).
 // Groups of 8 or more keep the matrix-core fixed kernel.
 // PAGEDATTN_SCHEDULE=fixed|stream forces either (stream only where it is
 // built).
-bool stream_eligible(int B, int Hkv, int G, int max_blocks, int bs, int requested) {
+bool stream_eligible(int B, int Hkv, int G, int D, int max_blocks, int bs, int requested) {
   if (requested != 0 || !stream_supported(G)) return false;
   if (B > kStreamMaxSeqs || max_blocks > 0xFFFF) return false;
   if (options().schedule == 1) return false;
   if (options().schedule == 2) return true;
   if ((int64_t)B * Hkv > kStreamWorkersAll) return false;
-  return G <= 2 || (G == 4 && (int64_t)max_blocks * bs <= 4096);
+  return G <= 2 || (G == 4 && D == 64 && (int64_t)max_blocks * bs <= 4096);
 }
 
 struct Plan {
@@ -143,7 +149,7 @@ bool make_plan(int B, int Hq, int Hkv, int D, int max_blocks, int bs, int reques
   p->stream = false;
   p->stream_workers = 0;
   if (B == 0) return true;
-  if (stream_eligible(B, Hkv, G, max_blocks, bs, requested)) {
+  if (stream_eligible(B, Hkv, G, D, max_blocks, bs, requested)) {
     // Workers per kv head: the aim, and enough that no range exceeds
     // kStreamMaxRange blocks however the lengths fall; a multiple of the
     // waves of a workgroup.
@@ -151,7 +157,7 @@ bool make_plan(int B, int Hq, int Hkv, int D, int max_blocks, int bs, int reques
                                                       : stream_workers_default(G);
     int64_t R = (all + Hkv - 1) / Hkv;
     R = std::max<int64_t>(R, ((int64_t)B * max_blocks + kStreamMaxRange - 1) / kStreamMaxRange);
-    R = (R + kStreamWaves - 1) / kStreamWaves * kStreamWaves;
+    R = (R + kStreamRangeQuantum - 1) / kStreamRangeQuantum * kStreamRangeQuantum;
     if (R * Hkv <= (int64_t)1 << 22) {
       p->stream = true;
       p->stream_workers = (int)R;

@@ -43,6 +43,13 @@ bool mfma_supported(int dtype, int D, int BS, int G);
 hipError_t launch_mfma(int D, int BS, int G, const DecodeArgs& a, hipStream_t s);
 
 constexpr int kStreamWaves = 4;  // worker waves per workgroup of the stream schedule
+// Waves per workgroup of the stream schedule's matrix-core worker: 8 at
+// head_dim 64, where a workgroup of eight fits the registers and LDS (the
+// Llama-3.2-shaped batch: 50.5 against 51.9 us with four), 4 at head_dim 128.
+__host__ __device__ constexpr int stream_mfma_waves(int D) { return D == 64 ? 8 : 4; }
+// Worker counts per kv head are rounded to a multiple of this, so that every
+// workgroup of either worker holds whole ranges.
+constexpr int kStreamRangeQuantum = 8;
 
 // Kv heads one stream workgroup takes (one wave each, over kStreamWaves / HW
 // consecutive ranges): as many as divide both the waves and the kv heads.

@@ -2,8 +2,9 @@
 // matrix-core worker: bfloat16, 4 query heads per kv head.
 //
 // The schedule is that of decode_stream.hip -- each kv head's block list cut
-// into equal ranges, one wave per range, four neighbouring kv heads per
-// workgroup, split sequences merged by the last piece to arrive -- and the
+// into equal ranges, one wave per range, up to four neighbouring kv heads
+// per workgroup over one or more consecutive ranges (eight waves at head_dim
+// 64, four at 128), split sequences merged by the last piece to arrive -- and the
 // fold of a block is that of the matrix-core decode (mfma_attn.hpp): the
 // wave stages the block's K and V rows of its kv head in its own LDS tile
 // and runs q.k and p.v as 16x16x32 MFMAs over its G query rows.  With four
@@ -26,25 +27,26 @@
 namespace pa {
 
 template <int D, int BS, int G, bool FUSED>
-__global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(stream_mfma_waves(D) * 64) void decode_stream_mfma_kernel(DecodeArgs a) {
+  constexpr int NW = stream_mfma_waves(D);
   using Sh = TileShape<D, BS, G>;
   using Tile = RowTileAttn<D, BS, G>;
   constexpr int RL = Sh::RL, ROWS = Sh::ROWS, NI = Sh::NI;
   constexpr int KPITCH = Sh::KPITCH, VPITCH = Sh::VPITCH;
   constexpr int KTILE = Sh::KTILE, VTILE = Sh::VTILE;
   constexpr int HT = Sh::HT, DK = Sh::DK, DT = Sh::DT;
-  constexpr int NT = kStreamWaves * 64;
+  constexpr int NT = NW * 64;
   constexpr int PF = 2;  // blocks in flight per wave
   static_assert(G == 4, "one 16-row tile of query heads, merged in one pass");
 
   __shared__ int s_cum[kStreamMaxSeqs + 1];
-  __shared__ int s_part[kStreamWaves];
-  __shared__ __attribute__((aligned(16))) char s_tile[kStreamWaves][KTILE + VTILE];
+  __shared__ int s_part[NW];
+  __shared__ __attribute__((aligned(16))) char s_tile[NW][KTILE + VTILE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Hkv = a.num_kv_heads, Hq = a.num_q_heads;
   const int HW = stream_heads_per_wg(Hkv);
-  const int RW = kStreamWaves / HW;
+  const int RW = NW / HW;
   const int ngr = Hkv / HW;
   const int gg = blockIdx.x % ngr, kwg = blockIdx.x / ngr;
   const int h = gg * HW + wave % HW;
@@ -280,14 +282,15 @@ bool stream_mfma_supported(int dtype, int G) { return dtype == PA_DTYPE_BF16 && 
 
 hipError_t launch_stream_mfma(int D, int BS, int G, const DecodeArgs& a, hipStream_t s) {
   const int HW = stream_heads_per_wg(a.num_kv_heads);
-  const dim3 grid((unsigned)(a.num_kv_heads / HW * (a.stream_workers / (kStreamWaves / HW))));
   const bool fused = a.new_k != nullptr;
   auto go = [&](auto d, auto bs, auto g) -> hipError_t {
     constexpr int Dv = decltype(d)::value, BSv = decltype(bs)::value, Gv = decltype(g)::value;
+    constexpr int NW = stream_mfma_waves(Dv);
+    const dim3 grid((unsigned)(a.num_kv_heads / HW * (a.stream_workers / (NW / HW))));
     if (fused)
-      decode_stream_mfma_kernel<Dv, BSv, Gv, true><<<grid, kStreamWaves * 64, 0, s>>>(a);
+      decode_stream_mfma_kernel<Dv, BSv, Gv, true><<<grid, NW * 64, 0, s>>>(a);
     else
-      decode_stream_mfma_kernel<Dv, BSv, Gv, false><<<grid, kStreamWaves * 64, 0, s>>>(a);
+      decode_stream_mfma_kernel<Dv, BSv, Gv, false><<<grid, NW * 64, 0, s>>>(a);
     return hipGetLastError();
   };
   if (G != 4) return hipErrorInvalidValue;

@@ -205,17 +205,19 @@ def test_partition_size_rule(lib):
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 16 * 129) == -1
     # left to the library: the balanced schedule (reported as 0) for at most
     # 1024 (sequence, kv head) pairs with 1 or 2 query heads per kv head, or
-    # 4 over tables of at most 4096 tokens; otherwise 1024 tokens at
-    # head_dim 128 (2048 for tables of more than 4096 tokens) and 1024 at
-    # head_dim 64 for groups of 4 or more
+    # 4 at head_dim 64 over tables of at most 4096 tokens; otherwise 1024
+    # tokens at head_dim 128 (2048 for tables of more than 4096 tokens) and
+    # 1024 at head_dim 64 for groups of 4 or more
     assert pa.decode_partition_size(32, 16, 8, 128, 128, 16, 0) == 0
     assert pa.decode_partition_size(64, 16, 8, 64, 256, 16, 0) == 0
     assert pa.decode_partition_size(4, 4, 2, 64, 4, 16, 0) == 0
     assert pa.decode_partition_size(64, 32, 8, 64, 256, 16, 0) == 0     # Llama-3.2 shape
-    assert pa.decode_partition_size(8, 32, 8, 128, 256, 16, 0) == 0
+    assert pa.decode_partition_size(64, 32, 8, 64, 128, 32, 0) == 0     # 32-token blocks
+    assert pa.decode_partition_size(64, 32, 8, 64, 257, 16, 0) == 1024  # > 4096 tokens
+    assert pa.decode_partition_size(8, 32, 8, 128, 256, 16, 0) == 1024  # G = 4 at D = 128
     assert pa.decode_partition_size(8, 32, 8, 128, 2048, 16, 0) == 2048  # 32K tokens
     assert pa.decode_partition_size(8, 32, 8, 128, 257, 16, 0) == 2048
-    assert pa.decode_partition_size(8, 32, 8, 128, 128, 32, 0) == 0     # 4096 tokens
+    assert pa.decode_partition_size(8, 32, 8, 128, 128, 32, 0) == 1024
     assert pa.decode_partition_size(8, 32, 8, 128, 129, 32, 0) == 2048
     assert pa.decode_partition_size(256, 32, 32, 128, 32, 32, 0) == 1024
     assert pa.decode_partition_size(256, 32, 8, 64, 256, 16, 0) == 1024  # 2048 pairs
