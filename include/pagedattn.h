@@ -286,7 +286,7 @@ pa_status pa_paged_attention_decode(void* out, const void* q,
  * positions, so its rows go to
  *     k_cache[block_tables[b, (L-1) / block_size], (L-1) % block_size, :, :] = key[b]
  * and the same for V -- exactly what pa_reshape_and_cache does with that
- * slot -- and the decode then reads them.  Out and caches are bit-identical
+ * slot -- and the decode attends them as position L-1.  Out and caches are bit-identical
  * to pa_reshape_and_cache (slot_mapping[b] = that slot) followed by
  * pa_paged_attention_decode with the same arguments; this saves the write's
  * launch.  Sequences with L == 0 or L past the table write nothing, nor does

@@ -39,8 +39,8 @@ struct DecodeArgs {
   int32_t stream_workers;  // stream schedule: worker waves per kv head (0: fixed partitions)
   float scale_log2;      // scale * log2(e): scores are kept in base-2 units
   // Decode step with the KV write fused in: this step's token of sequence b
-  // ([num_seqs, num_kv_heads, D] rows), written at position ctx - 1 before
-  // the partition holding it is read.  nullptr: the caches are only read.
+  // ([num_seqs, num_kv_heads, D] rows), attended as position ctx - 1 and
+  // written to that cache slot.  nullptr: the caches are only read.
   const void* new_k;
   const void* new_v;
 };
@@ -507,34 +507,71 @@ __device__ __forceinline__ bool partition_prologue(const DecodeArgs& a, int lane
   return true;
 }
 
-// Fused KV write of a decode step, by the workgroup of the partition that
-// holds position ctx - 1 (the step's token; called only there, uniformly):
-// the rows of its kv heads go from new_k / new_v to the cache slot the block
-// table gives for that position -- the slot a separate write would take --
-// unless that block lies outside the pool.  Only this workgroup reads those
-// rows in this launch; the barrier makes its stores visible to every wave's
-// loads that follow.
+// Fused KV write of a decode step on the fixed-partition schedule: the
+// step's token rows go from new_k / new_v ([num_seqs, num_kv_heads, D]) to
+// the cache slot the block table gives for position ctx - 1 -- the slot a
+// separate write would take -- unless the context is empty or out of range
+// or that block lies outside the pool.  The copy is done by extra
+// workgroups after the attention workgroups of the launch's last partition
+// row, so it runs in the launch's tail, when the K/V stream is draining:
+// stores issued by the attention workgroups themselves, interleaved with the
+// stream, cost far more than their bytes (on the 256-sequence MHA batch, 12
+// us for 4 MiB).  The attention workgroup of the token's partition takes the
+// new rows from new_k / new_v in registers, so it never needs the stored
+// copy, and a value it reads in that slot meanwhile is discarded.
+constexpr int kStepCopyChunks = 4;  // 16-byte chunks per thread
+
+__host__ __device__ inline int64_t step_copy_chunks(const DecodeArgs& a, int D, int elt_bytes) {
+  return (int64_t)a.num_seqs * 2 * a.num_kv_heads * D * elt_bytes / 16;
+}
+// Workgroups of NT threads that copy the step's rows (0 without a step),
+// rounded up to a multiple of 8: workgroups are dealt to the 8 XCDs
+// round-robin in linear-id order, so a grid row longer by a multiple of 8
+// leaves every attention workgroup on the XCD it has without a step (on the
+// 32K-token batch, 64 partition rows, any other count cost 1%).
+inline int step_copy_workgroups(const DecodeArgs& a, int D, int elt_bytes, int NT) {
+  if (a.new_k == nullptr) return 0;
+  const int64_t per_wg = (int64_t)NT * kStepCopyChunks;
+  const int64_t n = (step_copy_chunks(a, D, elt_bytes) + per_wg - 1) / per_wg;
+  return (int)((n + 7) / 8 * 8);
+}
+
+// Copy workgroup `wg`: chunks (wg * kStepCopyChunks + u) * NT + thread, in
+// order sequence, tensor (K, V), kv head, d.
 template <class DT, int D, int BS, int NT>
-__device__ __forceinline__ void write_step_token(const DecodeArgs& a, const PartitionWork& w) {
+__device__ __forceinline__ void step_copy(const DecodeArgs& a, int wg) {
   using S = typename DT::storage;
-  const int pos = w.ctx - 1;
-  const int blk = w.block(pos / BS - w.blk0);
-  if (blk >= 0 && blk < a.num_blocks) {
-    constexpr int kChunk = DT::kPerChunk;  // elements per 16-byte chunk
-    const int hpw = a.heads_per_wg;
-    const int chunks = hpw * D / kChunk;  // per tensor
-    const size_t src = ((size_t)w.b * a.num_kv_heads + (size_t)w.gg * hpw) * D;
-    const size_t dst =
-        (((size_t)blk * BS + pos % BS) * a.num_kv_heads + (size_t)w.gg * hpw) * D;
-    for (int c = threadIdx.x; c < 2 * chunks; c += NT) {
-      const bool is_v = c >= chunks;
-      const size_t off = (size_t)(is_v ? c - chunks : c) * kChunk;
-      const S* from = static_cast<const S*>(is_v ? a.new_v : a.new_k) + src + off;
-      S* to = static_cast<S*>(const_cast<void*>(is_v ? a.v_cache : a.k_cache)) + dst + off;
-      store_chunk(to, load_chunk(from));
-    }
+  constexpr int kChunk = DT::kPerChunk;  // elements per 16-byte chunk
+  const int row_chunks = a.num_kv_heads * D / kChunk;  // one tensor, one sequence
+  const int64_t total = step_copy_chunks(a, D, sizeof(S));
+#pragma unroll
+  for (int u = 0; u < kStepCopyChunks; ++u) {
+    const int64_t c = ((int64_t)wg * kStepCopyChunks + u) * NT + threadIdx.x;
+    if (c >= total) break;
+    const int b = (int)(c / (2 * row_chunks));
+    const int r = (int)(c - (int64_t)b * 2 * row_chunks);
+    const bool is_v = r >= row_chunks;
+    const int off = (is_v ? r - row_chunks : r) * kChunk;
+    const int ctx = a.context_lens[b];
+    if (ctx <= 0 || ctx > a.max_blocks * BS) continue;
+    const int blk = a.block_tables[(size_t)b * a.max_blocks + (ctx - 1) / BS];
+    if (blk < 0 || blk >= a.num_blocks) continue;
+    const size_t src = (size_t)b * a.num_kv_heads * D + off;
+    const size_t dst = ((size_t)blk * BS + (ctx - 1) % BS) * a.num_kv_heads * D + off;
+    store_chunk(static_cast<S*>(const_cast<void*>(is_v ? a.v_cache : a.k_cache)) + dst,
+                load_chunk(static_cast<const S*>(is_v ? a.new_v : a.new_k) + src));
   }
-  __syncthreads();
+}
+
+// In a fixed-partition kernel, before partition_prologue: true for the copy
+// workgroups (grid x past the attention workgroups), which do their share of
+// the copy in the last partition row and return.
+template <class DT, int D, int BS, int NT>
+__device__ __forceinline__ bool step_copy_role(const DecodeArgs& a) {
+  const int n_attn = a.num_seqs * (a.num_kv_heads / a.heads_per_wg);
+  if ((int)blockIdx.x < n_attn) return false;
+  if (blockIdx.y == gridDim.y - 1) step_copy<DT, D, BS, NT>(a, blockIdx.x - n_attn);
+  return true;
 }
 
 // End of a partition workgroup.  Every wave has left its state in LDS, one

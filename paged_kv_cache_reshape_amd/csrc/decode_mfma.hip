@@ -67,6 +67,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   const int hw = wave % hpw;
   const int tw = wave / hpw;
 
+  if (step_copy_role<BF16, D, BS, NT>(a)) return;
   T st;
   const QScale qs(a.scale_log2);
   PartitionWork w;
@@ -76,7 +77,6 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         st.load_q([&](int h) { return h < G ? q_grp + (size_t)h * D : nullptr; }, qs, lane);
       }))
     return;
-  if (a.new_k != nullptr && w.part == w.nparts - 1) write_step_token<BF16, D, BS, NT>(a, w);
   const int g = w.gg * hpw + hw;
   st.reset();
 
@@ -110,9 +110,33 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     for (int i = 0; i < NI; ++i)
       vr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off[i], 0, kLoadStreaming));
   };
+  // A decode step's new token (position ctx - 1, in the last partition):
+  // the wave that folds its block takes the step's K/V rows in place of what
+  // it read in that slot (the copy workgroups store them).  Rows past the
+  // context load the block's token 0, which is that slot when the new token
+  // opens its block (tt == 0): they take the new rows too, so that no stale
+  // value -- uninitialised memory, NaN included -- reaches a masked product.
+  const bool step = a.new_k != nullptr && w.part == w.nparts - 1;
+  const int tj = step ? (w.ctx - 1) / BS - w.blk0 : -1;  // block of the new token
+  const int tt = (w.ctx - 1) % BS, tli = tt / ROWS, tlr = tt % ROWS;
+  uint4 nk = make_uint4(0, 0, 0, 0), nv = nk;
+  if (step) {
+    const size_t src = ((size_t)w.b * Hkv + g) * D + col * 8;
+    nk = load_chunk(static_cast<const uint16_t*>(a.new_k) + src);
+    nv = load_chunk(static_cast<const uint16_t*>(a.new_v) + src);
+  }
   char* kt = s_raw + wave * (KTILE + VTILE);
   char* vt = kt + KTILE;
-  auto consume = [&](int jb, bool live, const uint4 (&kr)[NI], const uint4 (&vr)[NI]) {
+  auto consume = [&](int jb, bool live, uint4 (&kr)[NI], uint4 (&vr)[NI]) {
+    if (jb == tj) {
+#pragma unroll
+      for (int ii = 0; ii < NI; ++ii) {
+        if (tt == 0 || (ii == tli && row == tlr)) {
+          kr[ii] = nk;
+          vr[ii] = nv;
+        }
+      }
+    }
     // Stage the block (this wave's tile only; LDS keeps one wave's accesses
     // in order, so the reads below see these writes).
 #pragma unroll
@@ -151,7 +175,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 
 template <int D, int BS, int G>
 hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.num_seqs * (a.num_kv_heads / a.heads_per_wg), a.max_parts);
+  const int copy_wgs = step_copy_workgroups(a, D, 2, kGroupWaves * 64);
+  dim3 grid(a.num_seqs * (a.num_kv_heads / a.heads_per_wg) + copy_wgs, a.max_parts);
   decode_mfma_kernel<D, BS, G, kGroupWaves><<<grid, kGroupWaves * 64, 0, stream>>>(a);
   return hipGetLastError();
 }

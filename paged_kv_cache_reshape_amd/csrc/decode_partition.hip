@@ -40,6 +40,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
   const int row = lane / RL;
   const int col = lane % RL;
 
+  if (step_copy_role<DT, D, BS, NT>(a)) return;
   Row st;
   PartitionWork w;
   if (!partition_prologue<DT, D, BS, G, NT>(a, lane, w, [&](int b, int gg) {
@@ -48,7 +49,6 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
                   col);
       }))
     return;
-  if (a.new_k != nullptr && w.part == w.nparts - 1) write_step_token<DT, D, BS, NT>(a, w);
   const int g = w.gg * hpw + hw;
   const int ctx = w.ctx, blk0 = w.blk0;
 
@@ -79,7 +79,31 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
       vr[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                             rv, lane_bytes + t * ROWS * tok_bytes, 0, kLoadNT));
   };
-  auto consume = [&](int j, bool live, const uint4 (&kr)[NI], const uint4 (&vr)[NI]) {
+  // A decode step's new token (position ctx - 1, in the last partition):
+  // the wave that folds its block takes the step's K/V rows in place of what
+  // it read in that slot (the copy workgroups store them).  Rows past the
+  // context load the block's token 0, which is that slot when the new token
+  // opens its block (tt == 0): they take the new rows too, so that no stale
+  // value -- uninitialised memory, NaN included -- reaches a masked product.
+  const bool step = a.new_k != nullptr && w.part == w.nparts - 1;
+  const int tj = step ? (ctx - 1) / BS - blk0 : -1;  // block of the new token
+  const int tt = (ctx - 1) % BS, tli = tt / ROWS, tlr = tt % ROWS;
+  uint4 nk = make_uint4(0, 0, 0, 0), nv = nk;
+  if (step) {
+    const size_t src = ((size_t)w.b * Hkv + g) * D + col * E;
+    nk = load_chunk(static_cast<const S*>(a.new_k) + src);
+    nv = load_chunk(static_cast<const S*>(a.new_v) + src);
+  }
+  auto consume = [&](int j, bool live, uint4 (&kr)[NI], uint4 (&vr)[NI]) {
+    if (j == tj) {
+#pragma unroll
+      for (int ii = 0; ii < NI; ++ii) {
+        if (tt == 0 || (ii == tli && row == tlr)) {
+          kr[ii] = nk;
+          vr[ii] = nv;
+        }
+      }
+    }
     st.consume((blk0 + j) * BS + row, ctx, live, a.scale_log2, kr, vr);
   };
   stream_blocks<NI>(tw, nwt, w.nblk_run, fetch, consume);
@@ -101,7 +125,9 @@ __global__ __launch_bounds__(NT) void merge_partitions_kernel(DecodeArgs a, int 
 
 template <class DT, int D, int BS, int G>
 hipError_t launch_partition_t(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.num_seqs * (a.num_kv_heads / a.heads_per_wg), a.max_parts);
+  constexpr int NT = kDecodeWaves * 64;
+  const int copy_wgs = step_copy_workgroups(a, D, sizeof(typename DT::storage), NT);
+  dim3 grid(a.num_seqs * (a.num_kv_heads / a.heads_per_wg) + copy_wgs, a.max_parts);
   decode_partition_kernel<DT, D, BS, G, kDecodeWaves><<<grid, kDecodeWaves * 64, 0, stream>>>(a);
   return hipGetLastError();
 }

@@ -502,6 +502,41 @@ def test_decode_step_equals_write_then_decode(name, ps):
     assert np.array_equal(G.host_storage(d2["v_cache"]), v_ref)
 
 
+@pytest.mark.parametrize("name,ps", [("qwen3_0p6b", 0), ("qwen3_0p6b", 64), ("tiny_f32", 0),
+                                     ("llama32_1b", 0), ("bf16_d64_bs32_g8", 0),
+                                     ("bf16_d64_bs32_g32", 96), ("f32_d128_bs32_g4", 64),
+                                     ("mha_large", 0), ("mqa_large", 0)])
+def test_decode_step_target_slot_holds_nan(name, ps):
+    """The slot a step writes holds anything beforehand (a fresh block is
+    uninitialised memory): NaN there changes no bit of the fused step's output,
+    also where the new token is the first of its block, whose rows past the
+    context load that slot and are masked; afterwards both caches equal the
+    separate write's.  Every schedule and kernel family, full-size batches
+    included (the fixed kernels copy the rows in extra workgroups that may
+    run while the token's partition reads the slot)."""
+    base = inputs_for(name)
+    w = base["workload"]
+    bs = w.block_size
+    ctx = base["context_lens"].copy()
+    ctx[0], ctx[1] = bs + 1, 1                   # new token first in its block
+    if len(ctx) > 2:
+        ctx[2] = min(2 * bs + 1, w.max_blocks_per_seq * bs)
+    inp = inputs_for(name, context_lens=ctx)
+    say("fused step, NaN in the target slot", name, ps)
+    d1, d2 = G.upload(inp), G.upload(inp)
+    want = G.host_storage(gpu_step(d1, ps))
+    nan = torch.tensor(float("nan"), dtype=d2["k_cache"].dtype, device="cuda")
+    slots = torch.from_numpy(inp["slot_mapping"]).cuda()
+    slots = slots[slots >= 0]
+    for c in ("k_cache", "v_cache"):
+        flat = d2[c].view(-1, *d2[c].shape[2:])
+        flat[slots] = nan
+    got = G.host_storage(fused_step(d2, ps))
+    assert np.array_equal(got, want)
+    for c in ("k_cache", "v_cache"):
+        assert torch.equal(d1[c], d2[c]), c
+
+
 def test_decode_step_edge_sequences():
     """Empty sequences, a new token whose block lies outside the pool and a
     length past the table write nothing; their rows are what the decode
