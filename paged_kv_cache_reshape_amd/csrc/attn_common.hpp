@@ -507,18 +507,18 @@ __device__ __forceinline__ bool partition_prologue(const DecodeArgs& a, int lane
   return true;
 }
 
-// Fused KV write of a decode step on the fixed-partition schedule: the
+// Fused KV write of a decode step: the
 // step's token rows go from new_k / new_v ([num_seqs, num_kv_heads, D]) to
 // the cache slot the block table gives for position ctx - 1 -- the slot a
 // separate write would take -- unless the context is empty or out of range
 // or that block lies outside the pool.  The copy is done by extra
-// workgroups after the attention workgroups of the launch's last partition
-// row, so it runs in the launch's tail, when the K/V stream is draining:
-// stores issued by the attention workgroups themselves, interleaved with the
-// stream, cost far more than their bytes (on the 256-sequence MHA batch, 12
-// us for 4 MiB).  The attention workgroup of the token's partition takes the
-// new rows from new_k / new_v in registers, so it never needs the stored
-// copy, and a value it reads in that slot meanwhile is discarded.
+// workgroups after the attention workgroups (of the last partition row on
+// the fixed schedule), the last ones dispatched: stores issued by the
+// attention workgroups themselves, interleaved with the stream, cost far
+// more than their bytes (on the 256-sequence MHA batch, 12 us for 4 MiB).
+// The wave that attends the token takes the new rows from new_k / new_v in
+// registers, so it never needs the stored copy, and a value it reads in
+// that slot meanwhile is discarded.
 constexpr int kStepCopyChunks = 4;  // 16-byte chunks per thread
 
 __host__ __device__ inline int64_t step_copy_chunks(const DecodeArgs& a, int D, int elt_bytes) {
@@ -563,12 +563,11 @@ __device__ __forceinline__ void step_copy(const DecodeArgs& a, int wg) {
   }
 }
 
-// In a fixed-partition kernel, before partition_prologue: true for the copy
-// workgroups (grid x past the attention workgroups), which do their share of
-// the copy in the last partition row and return.
+// At the start of a decode kernel whose first n_attn workgroups (in grid x)
+// attend: true for the copy workgroups after them, which do their share of
+// the copy in the grid's last row and return.
 template <class DT, int D, int BS, int NT>
-__device__ __forceinline__ bool step_copy_role(const DecodeArgs& a) {
-  const int n_attn = a.num_seqs * (a.num_kv_heads / a.heads_per_wg);
+__device__ __forceinline__ bool step_copy_role(const DecodeArgs& a, int n_attn) {
   if ((int)blockIdx.x < n_attn) return false;
   if (blockIdx.y == gridDim.y - 1) step_copy<DT, D, BS, NT>(a, blockIdx.x - n_attn);
   return true;

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   const int hw = wave % hpw;
   const int tw = wave / hpw;
 
-  if (step_copy_role<BF16, D, BS, NT>(a)) return;
+  if (step_copy_role<BF16, D, BS, NT>(a, a.num_seqs * (a.num_kv_heads / a.heads_per_wg))) return;
   T st;
   const QScale qs(a.scale_log2);
   PartitionWork w;

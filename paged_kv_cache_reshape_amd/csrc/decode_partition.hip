@@ -40,7 +40,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
   const int row = lane / RL;
   const int col = lane % RL;
 
-  if (step_copy_role<DT, D, BS, NT>(a)) return;
+  if (step_copy_role<DT, D, BS, NT>(a, a.num_seqs * (a.num_kv_heads / a.heads_per_wg))) return;
   Row st;
   PartitionWork w;
   if (!partition_prologue<DT, D, BS, G, NT>(a, lane, w, [&](int b, int gg) {

@@ -10,9 +10,10 @@
 // loads, two blocks in flight), the query rows of the block's sequence (a
 // 512-byte read that hits the L2 after the sequence's first block) and, in a
 // decode step, the step's new K/V rows.  In a decode step the block holding
-// position ctx - 1 takes the new rows in place of what it read there, and the
-// wave writes them to the cache -- nothing else in the launch reads that row,
-// so the result is the write followed by the read, bit for bit.
+// position ctx - 1 takes the new rows in place of what it read there; copy
+// workgroups after the workers store them (step_copy): nothing in the launch
+// reads the stored copy, so the result is the write followed by the read,
+// bit for bit.
 #include "stream_sched.hpp"
 
 #include "decode_launch.hpp"
@@ -49,6 +50,11 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Hkv = a.num_kv_heads, Hq = a.num_q_heads;
+  if constexpr (FUSED) {
+    const int hw = stream_heads_per_wg(Hkv);
+    if (step_copy_role<DT, D, BS, NT>(a, Hkv / hw * (a.stream_workers / (kStreamWaves / hw))))
+      return;
+  }
   // The workgroup's waves take HW neighbouring kv heads (one each) of RW
   // consecutive ranges: their loads then cover HW * D * elt contiguous bytes
   // of each token row, which measured far steadier per-wave rates than waves
@@ -212,7 +218,6 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
     // Everything read back from the lanes (readlane) is read here, with every
     // lane active: a value selected per lane inside a divergent branch is not
     // defined in the inactive lanes readlane would read.
-    const int id = w.entry(i);
     const int v = w.seqblk(i);
     const int b = (v >> 16) & 0x7FFF, j = v & 0xFFFF;
     const bool bad = v < 0;
@@ -236,12 +241,6 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
             sl.k[ii] = sl.nk;
             sl.v[ii] = sl.nv;
           }
-        }
-        if (!bad && row == lr) {
-          const size_t dst =
-              (size_t)id * blk_stride + (size_t)t * tok_stride + (size_t)h * D + col * E;
-          store_chunk(static_cast<S*>(const_cast<void*>(a.k_cache)) + dst, sl.nk);
-          store_chunk(static_cast<S*>(const_cast<void*>(a.v_cache)) + dst, sl.nv);
         }
       }
     }
@@ -334,11 +333,14 @@ hipError_t launch_stream_merge(int dtype, int D, int BS, int G, const DecodeArgs
 
 hipError_t launch_stream(int dtype, int D, int BS, int G, const DecodeArgs& a, hipStream_t s) {
   const int HW = stream_heads_per_wg(a.num_kv_heads);
-  const dim3 grid((unsigned)(a.num_kv_heads / HW * (a.stream_workers / (kStreamWaves / HW))));
   const bool fused = a.new_k != nullptr;
   auto go = [&](auto dt, auto d, auto bs, auto g) -> hipError_t {
     using DT = decltype(dt);
     constexpr int Dv = decltype(d)::value, BSv = decltype(bs)::value, Gv = decltype(g)::value;
+    const int copy_wgs =
+        step_copy_workgroups(a, Dv, sizeof(typename DT::storage), kStreamWaves * 64);
+    const dim3 grid(
+        (unsigned)(a.num_kv_heads / HW * (a.stream_workers / (kStreamWaves / HW)) + copy_wgs));
     if (fused)
       decode_stream_kernel<DT, Dv, BSv, Gv, true><<<grid, kStreamWaves * 64, 0, s>>>(a);
     else

@@ -16,9 +16,9 @@
 // anything, and a zero weight times a NaN value would still be NaN); a block
 // whose table entry lies outside the pool is read from block 0, zeroed and
 // marks its sequence's rows NaN.  In a decode step the block holding
-// position ctx - 1 takes the step's new rows in place of what it read there,
-// and the wave writes them to the cache (nothing else in the launch reads
-// that row).
+// position ctx - 1 takes the step's new rows in place of what it read there;
+// copy workgroups after the workers store them (step_copy), and nothing in
+// the launch reads the stored copy.
 #include "mfma_attn.hpp"
 #include "stream_sched.hpp"
 
@@ -48,6 +48,9 @@ __global__ __launch_bounds__(stream_mfma_waves(D) * 64) void decode_stream_mfma_
   const int HW = stream_heads_per_wg(Hkv);
   const int RW = NW / HW;
   const int ngr = Hkv / HW;
+  if constexpr (FUSED) {
+    if (step_copy_role<BF16, D, BS, NT>(a, ngr * (a.stream_workers / RW))) return;
+  }
   const int gg = blockIdx.x % ngr, kwg = blockIdx.x / ngr;
   const int h = gg * HW + wave % HW;
   const int wgs_per_group = a.stream_workers / RW;
@@ -191,7 +194,6 @@ __global__ __launch_bounds__(stream_mfma_waves(D) * 64) void decode_stream_mfma_
   auto consume = [&](int i, Slot& sl) {
     // Everything read back from the lanes (readlane) is read here, with every
     // lane active.
-    const int id = w.entry(i);
     const int v = w.seqblk(i);
     const int b = (v >> 16) & 0x7FFF, j = v & 0xFFFF;
     const bool bad = v < 0;
@@ -219,11 +221,6 @@ __global__ __launch_bounds__(stream_mfma_waves(D) * 64) void decode_stream_mfma_
             sl.k[ii] = sl.nk;
             sl.v[ii] = sl.nv;
           }
-        }
-        if (!bad && row == lr) {
-          const size_t dst = (size_t)id * blk_bytes + (size_t)t * tok_bytes + head_off;
-          store_chunk(static_cast<char*>(const_cast<void*>(a.k_cache)) + dst, sl.nk);
-          store_chunk(static_cast<char*>(const_cast<void*>(a.v_cache)) + dst, sl.nv);
         }
       }
     }
@@ -286,7 +283,8 @@ hipError_t launch_stream_mfma(int D, int BS, int G, const DecodeArgs& a, hipStre
   auto go = [&](auto d, auto bs, auto g) -> hipError_t {
     constexpr int Dv = decltype(d)::value, BSv = decltype(bs)::value, Gv = decltype(g)::value;
     constexpr int NW = stream_mfma_waves(Dv);
-    const dim3 grid((unsigned)(a.num_kv_heads / HW * (a.stream_workers / (NW / HW))));
+    const int copy_wgs = step_copy_workgroups(a, Dv, 2, NW * 64);
+    const dim3 grid((unsigned)(a.num_kv_heads / HW * (a.stream_workers / (NW / HW)) + copy_wgs));
     if (fused)
       decode_stream_mfma_kernel<Dv, BSv, Gv, true><<<grid, NW * 64, 0, s>>>(a);
     else
