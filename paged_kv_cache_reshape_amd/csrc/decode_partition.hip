@@ -118,9 +118,9 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
                                                   w.poisoned, s_acc, s_m, s_l);
 }
 
-template <class DT, int D, int G, int NT>
-__global__ __launch_bounds__(NT) void merge_partitions_kernel(DecodeArgs a, int bs) {
-  merge_partitions<DT, D, G, NT>(a, bs);
+template <class DT, int D, int G>
+__global__ __launch_bounds__(D) void merge_partitions_kernel(DecodeArgs a, int bs) {
+  merge_partitions<DT, D, G>(a, bs);
 }
 
 template <class DT, int D, int BS, int G>
@@ -134,8 +134,9 @@ hipError_t launch_partition_t(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_merge(int dtype, int D, int BS, int G, const DecodeArgs& a, hipStream_t s) {
   return dispatch_decode(dtype, D, 16, G, [&](auto dt, auto d, auto, auto g) {
-    merge_partitions_kernel<decltype(dt), decltype(d)::value, decltype(g)::value, 256>
-        <<<a.num_seqs * a.num_kv_heads, 256, 0, s>>>(a, BS);
+    constexpr int Dv = decltype(d)::value;
+    merge_partitions_kernel<decltype(dt), Dv, decltype(g)::value>
+        <<<a.num_seqs * a.num_q_heads, Dv, 0, s>>>(a, BS);
     return hipGetLastError();
   });
 }
