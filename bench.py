@@ -172,6 +172,65 @@ def gather_then_sdpa(q, k_cache, v_cache, block_tables, context_lens, scale):
     return out.reshape(B, hq, d).to(q.dtype)
 
 
+def stream_probe(torch, per_wg_bytes: int = 4 << 20) -> dict:
+    """HBM streaming rates of plain reads (read_ceiling.hip rc_stream_probe):
+    8, 64 and 256 workgroups, each streaming its own 4 MiB with 8 16-byte
+    loads per lane in flight (8 waves: 64 KiB per workgroup; 16 waves: 128
+    KiB), non-temporal and plain.  Workgroups are dealt to the 8 XCDs in
+    turn, so 8 puts one reading CU on each XCD and 256 one on every CU.
+    Every launch reads a region that no earlier launch of the probe read
+    (the 2 GiB buffer is 8x the last-level cache; at 256 workgroups each
+    launch reads 1 GiB); the median of the last 3 of 4 launches is reported."""
+    import ctypes
+    path = os.path.join(ROOT, "libreadceiling.so")
+    if not os.path.exists(path):
+        from paged_kv_cache_reshape_amd import build as _b
+        _b.build_read_ceiling()
+    lib = ctypes.CDLL(path)
+    f = lib.rc_stream_probe
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    total = 2 << 30
+    buf = torch.randint(0, 1 << 30, (total // 4,), dtype=torch.int32, device=dev)
+    sink = torch.zeros(2048, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    per_wg = per_wg_bytes // 16
+    u = 8
+    rows = []
+    for nwg in (8, 64, 256):
+        span = nwg * per_wg_bytes
+        nregions = total // span
+        k = 0
+        for threads in (512, 1024):
+            for nt in (1, 0):
+                times = []
+                for rep in range(4):
+                    off = (k % nregions) * span
+                    k += 1
+                    assert off + span <= total
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    torch.cuda.synchronize()
+                    e0.record(stream)
+                    st = f(buf.data_ptr() + off, per_wg, nwg, threads, u, nt, sink.data_ptr(),
+                           stream.cuda_stream)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    if st != 0:
+                        raise RuntimeError(f"rc_stream_probe: status {st}")
+                    times.append(e0.elapsed_time(e1) * 1e3)
+                t = float(np.median(times[1:]))
+                rows.append({"workgroups": nwg, "waves": threads // 64,
+                             "in_flight_kib": threads * u * 16 // 1024, "non_temporal": bool(nt),
+                             "us": round(t, 1), "per_cu_gbs": round(per_wg_bytes / t / 1e3, 1),
+                             "total_tbs": round(span / t / 1e6, 2)})
+    return {"kind": "HBM streaming probe (read_ceiling.hip rc_stream_probe): each workgroup "
+                    "streams its own 4 MiB, cold", "rows": rows}
+
+
 def read_ceilings(torch, w, inp, kcs, vcs, tables, lens, stream, n: int):
     """Mean µs per launch of the pure-read kernels of ``read_ceiling.hip``
     (same bytes as the decode's K/V reads, no arithmetic) over n launches
@@ -522,6 +581,9 @@ def main() -> int:
     ap.add_argument("--step-only", action="store_true",
                     help="time the steps only (no separate decode, write or graph timing), "
                          "so that every decode-kernel launch is a fused step: for counter runs")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="print the HBM streaming rates of 8, 64 and 256 reading workgroups "
+                         "(read_ceiling.hip rc_stream_probe) as JSON and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -537,6 +599,10 @@ def main() -> int:
             base = cpu_baseline(synth.make_inputs(synth.WORKLOADS[args.workload]),
                                 args.cpu_seconds)
         print(json.dumps(base), flush=True)
+        return 0
+    if args.stream_probe:
+        import torch
+        print(json.dumps(stream_probe(torch)), flush=True)
         return 0
     # The CPU baseline runs first, in a child process, before anything here
     # touches the GPU.

@@ -23,9 +23,16 @@
 //
 // bfloat16 caches, head_dim 64 or 128, block_size 16 or 32, at most 2048
 // sequences and 128 blocks per range.
+//
+// rc_stream_probe: the rate of plain streaming reads -- nwg workgroups, each
+// reading its own contiguous per_wg-vector region, U 16-byte loads per lane
+// in flight, non-temporal or plain -- to see what one CU, some CUs and every
+// CU draw from HBM.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace {
 
@@ -274,6 +281,34 @@ __global__ __launch_bounds__(512) void read_token_rows(Args a) {
 // caches must hold at least that.  sink: >= 2048 uint32 of device memory.
 // Returns 0, or -1 for sizes the kernels are not built for (nothing is
 // launched), or the HIP error of the launch.
+// Stream probe: workgroup g reads vectors [g per_wg, (g + 1) per_wg) of p.
+template <int U, bool NT>
+__global__ void stream_probe(const uint4* __restrict__ p, long per_wg, uint32_t* sink) {
+  const uint4* base = p + (long)blockIdx.x * per_wg;
+  uint32_t acc = 0;
+  const long nt = blockDim.x;
+  for (long i = threadIdx.x; i < per_wg; i += nt * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long j = i + u * nt;
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (j < per_wg) {
+        if constexpr (NT) {
+          typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+          const u4 t = __builtin_nontemporal_load(reinterpret_cast<const u4*>(base + j));
+          v[u] = make_uint4(t.x, t.y, t.z, t.w);
+        } else {
+          v[u] = base[j];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x & 2047] = acc;  // keeps the loads alive
+}
+
 extern "C" int rc_read_ceiling(int mode, const void* k_cache, const void* v_cache,
                                const int* block_tables, const int* context_lens, int num_seqs,
                                int max_blocks, int num_kv_heads, int head_dim, int block_size,
@@ -339,4 +374,29 @@ extern "C" int rc_read_ceiling(int mode, const void* k_cache, const void* v_cach
   }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? 0 : (int)e;
+}
+
+// nwg workgroups of `threads` threads stream per_wg 16-byte vectors each from
+// p (which holds nwg * per_wg); u in {1, 2, 4, 8, 16} loads in flight per
+// lane; nt: non-temporal loads.  Returns 0, -1 for arguments it does not
+// take, or the HIP error of the launch.
+extern "C" int rc_stream_probe(const void* p, long long per_wg, int nwg, int threads, int u,
+                               int nt, uint32_t* sink, void* stream) {
+  if (nwg < 1 || per_wg < 1 || threads < 64 || threads > 1024 || threads % 64) return -1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint4* v = static_cast<const uint4*>(p);
+  auto go = [&](auto uc, auto ntc) {
+    stream_probe<decltype(uc)::value, decltype(ntc)::value><<<nwg, threads, 0, s>>>(v, per_wg, sink);
+    return (int)hipGetLastError();
+  };
+  using F = std::integral_constant<bool, false>;
+  using T = std::integral_constant<bool, true>;
+  switch (u) {
+    case 1: return nt ? go(std::integral_constant<int, 1>{}, T{}) : go(std::integral_constant<int, 1>{}, F{});
+    case 2: return nt ? go(std::integral_constant<int, 2>{}, T{}) : go(std::integral_constant<int, 2>{}, F{});
+    case 4: return nt ? go(std::integral_constant<int, 4>{}, T{}) : go(std::integral_constant<int, 4>{}, F{});
+    case 8: return nt ? go(std::integral_constant<int, 8>{}, T{}) : go(std::integral_constant<int, 8>{}, F{});
+    case 16: return nt ? go(std::integral_constant<int, 16>{}, T{}) : go(std::integral_constant<int, 16>{}, F{});
+  }
+  return -1;
 }
