@@ -563,7 +563,12 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
+    # Untimed steps before the timed ones.  The GPU's clocks take longer than
+    # 50 steps to settle after the idle CPU-baseline phase: measured on
+    # MI355X, 50 warm-up steps left the timed Qwen3 steps at 33.0 us and the
+    # Llama-3.2 ones at 52.0 us, against 32.7 and 50.7 us after 3000 (the
+    # decode loops timed later in the same run read the same either way).
+    ap.add_argument("--warmup", type=int, default=3000)
     ap.add_argument("--workload", default="qwen3_0p6b",
                     choices=sorted(synth.WORKLOADS) + sorted(synth.PREFILL_WORKLOADS),
                     help="a decode batch, or a prefill batch (prefill_*, chunked_*)")
