@@ -650,7 +650,7 @@ def main() -> int:
     out = torch.empty_like(q)
     hq, hkv, d, bs = w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
     ws_bytes = pa.decode_workspace_bytes(w.num_seqs, hq, hkv, d, tables.shape[1], bs, ps)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     counters = torch.zeros(w.num_seqs * hkv, dtype=torch.int32, device=dev)
     part = pa.decode_partition_size(w.num_seqs, hq, hkv, d, tables.shape[1], bs, ps)
 

@@ -208,9 +208,11 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
  * head_dim floats of unnormalised output plus the running max and sum.  With
  * fixed partitions, one piece per (sequence, KV head, partition); with the
  * balanced schedule, two per (KV head, worker range).  0 when no sequence
- * can span more than one piece, and 0 on invalid sizes.  The workspace needs
- * no initialisation.  Two calls that may run at the same time must not share
- * a workspace.
+ * can span more than one piece, and 0 on invalid sizes.  The workspace must
+ * be all zero before its first use (like the counters); every call leaves
+ * what it used at zero again, so one workspace serves any later call (any
+ * sizes) on the same stream.  Two calls that may run at the same time must
+ * not share a workspace.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim,
@@ -245,9 +247,11 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * launch).  Under the balanced schedule (partition size 0 from
  * pa_decode_partition_size) each KV head's blocks, sequence after sequence,
  * are cut into equal ranges, one per worker; a sequence cut by a range
- * boundary is merged the same way by the last of its pieces to finish.
- * Results do not depend on the order in which partitions finish
- * (bit-identical reruns).
+ * boundary is merged in the same launch by the worker holding its last
+ * block, which waits for the other pieces' states to land (they belong to
+ * workgroups dispatched no later than its own; the wait is bounded, so it
+ * cannot hang); that schedule uses no arrival counters.  Results do not
+ * depend on the order in which partitions finish (bit-identical reruns).
  *
  *   out            [num_seqs, num_q_heads, head_dim]                   (written)
  *   q              [num_seqs, num_q_heads, head_dim]                   (read)
@@ -255,7 +259,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *   block_tables   [num_seqs, max_blocks_per_seq] int32                (read)
  *   context_lens   [num_seqs] int32                                    (read)
  *   workspace      >= pa_decode_workspace_bytes(...) bytes, 256-byte
- *                  aligned, contents ignored (NULL allowed if that size is 0)
+ *                  aligned, all zero before the first call; every call
+ *                  leaves it all zero again (NULL allowed if that size is 0)
  *   counters       >= num_seqs * num_kv_heads int32 arrival counters; all
  *                  zero before the first call; every call leaves the
  *                  counters it used at zero again, so one counter array can
@@ -319,7 +324,7 @@ pa_status pa_decode_step(void* out, const void* q, const void* key, const void* 
  * allocated: the caller passes every input and `out`.
  *
  * The device of `stream` must be current.  The first call on a device finds
- * that device's buffer and clears its counters with a kernel on `stream`; it
+ * that device's buffer and clears it with a kernel on `stream`; it
  * must not be made under graph capture (PA_ERR_INVALID_ARGUMENT).  Every call
  * on one GPU shares that GPU's buffer, which keeps the last call's contents:
  * calls that may overlap on one GPU (other streams, other host threads) race

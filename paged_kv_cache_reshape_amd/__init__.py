@@ -221,17 +221,17 @@ _counters: dict = {}
 
 def workspace_for(device: torch.device, nbytes: int,
                   stream: int | None = None) -> torch.Tensor | None:
-    """A workspace of >= nbytes for this device and current stream (cached).
-
-    Its contents need no initialisation; it is reused by later calls on the
-    same stream and replaced by a larger one when needed.
+    """A zero-initialised workspace of >= nbytes for this device and current
+    stream (cached).  Every decode call leaves the workspace it used at zero,
+    so it is reused by later calls on the same stream, whatever their sizes,
+    and replaced by a larger one when needed.
     """
     if nbytes == 0:
         return None
     key = (device.index, _stream(device) if stream is None else stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -326,8 +326,8 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                            counters: torch.Tensor | None = None) -> torch.Tensor:
     """Decode attention ``out[B, Hq, D]`` over the paged caches.
 
-    ``workspace`` (uint8, contents ignored) and ``counters`` (int32, all zero
-    before first use, kept zero by every call) default to per-stream buffers
+    ``workspace`` (uint8) and ``counters`` (int32), both all zero before
+    first use and kept zero by every call, default to per-stream buffers
     managed here.
     """
     return _decode_call(q, k_cache, v_cache, block_tables, context_lens, scale, partition_size,

@@ -141,6 +141,34 @@ struct CoherentRegion {
   __device__ __forceinline__ void store1(uint32_t off, float a) const {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), r, off, 0, kSystemCoherent);
   }
+  // Raw 32-bit words (encoded partial states of the balanced schedule).
+  __device__ __forceinline__ void store4u(uint32_t off, const uint32_t* w) const {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    const u4 v = {w[0], w[1], w[2], w[3]};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kSystemCoherent);
+  }
+  __device__ __forceinline__ void store2u(uint32_t off, uint32_t a, uint32_t b) const {
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    const u2 v = {a, b};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kSystemCoherent);
+  }
+  // N consecutive words (N in {2, 4, 8, 16}) at byte offset off.
+  template <int N>
+  __device__ __forceinline__ void loadu(uint32_t off, uint32_t* w) const {
+    if constexpr (N == 2) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kSystemCoherent);
+      w[0] = v[0];
+      w[1] = v[1];
+    } else {
+      static_assert(N % 4 == 0, "whole 16-byte pieces");
+#pragma unroll
+      for (int k = 0; k < N / 4; ++k) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * k, 0, kSystemCoherent);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) w[4 * k + t] = v[t];
+      }
+    }
+  }
   // N consecutive floats (N in {1, 2, 4, 8, 16}) at byte offset off.
   template <int N>
   __device__ __forceinline__ void load(uint32_t off, float* x) const {
@@ -420,6 +448,22 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int npieces, i
   for (int k = 0; k < EPT; ++k) {
     const int e = tid + k * NT;
     if (e < elems) store_out(DT{}, a.out, out_base + e, rA[k] / rL[k]);
+  }
+  // Leave the workspace zero, as the balanced schedule's merges expect it:
+  // each thread zeroes the words it loaded, now that it has used them, with
+  // ordinary stores (nothing in this launch reads them again, and the end of
+  // the launch writes them back before any later launch reads them).
+  for (int pc = 0; pc < npieces; ++pc) {
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) a.ws_acc[row_of(pc, qh[k]) * D + dd[k]] = 0.0f;
+  }
+  for (int c0 = 0; c0 < npieces; c0 += kChunk) {
+    const int n = min(kChunk, npieces - c0);
+    for (int i = tid; i < n * gh; i += NT) {
+      const size_t r = row_of(c0 + i / gh, i % gh);
+      a.ws_ml[r * 2] = 0.0f;
+      a.ws_ml[r * 2 + 1] = 0.0f;
+    }
   }
 }
 

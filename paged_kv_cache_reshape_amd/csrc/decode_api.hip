@@ -219,9 +219,11 @@ static __device__ __align__(256) unsigned char
 
 namespace {
 
-__global__ void __launch_bounds__(256) zero_counters(int32_t* c, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) c[i] = 0;
+// Zero n 16-byte words (the counters, then the workspace, which the merges
+// expect all zero and leave all zero).
+__global__ void __launch_bounds__(256) zero_scratch(uint4* c, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    c[i] = make_uint4(0, 0, 0, 0);
 }
 
 constexpr int kMaxDevices = 64;
@@ -229,7 +231,7 @@ std::mutex g_scratch_mutex;
 char* g_scratch[kMaxDevices];  // per device: the address of its `scratch`
 
 // The current device's `scratch`.  The first call on a device looks the
-// address up and clears the counters with a fill kernel on `s` (a kernel,
+// address up and clears it with a fill kernel on `s` (a kernel,
 // not a memset, so that the clear is an ordinary stream operation); that
 // call must not be captured into a graph, since the graph's replays would be
 // the only runs of the clear.
@@ -260,11 +262,12 @@ pa_status scratch_on_current_device(hipStream_t s, char** out) {
                 hipGetErrorString(e));
       return PA_ERR_HIP;
     }
-    zero_counters<<<dim3((unsigned)(kScratchCounters / 256)), dim3(256), 0, s>>>(
-        static_cast<int32_t*>(p), (int)kScratchCounters);
+    static_assert((kScratchCounterBytes + kScratchWorkspaceBytes) % 16 == 0, "whole 16-byte words");
+    zero_scratch<<<dim3(1024), dim3(256), 0, s>>>(
+        static_cast<uint4*>(p), (kScratchCounterBytes + kScratchWorkspaceBytes) / 16);
     e = hipGetLastError();
     if (e != hipSuccess) {
-      set_error("clearing the scratch counters failed: %s", hipGetErrorString(e));
+      set_error("clearing the scratch buffer failed: %s", hipGetErrorString(e));
       return PA_ERR_HIP;
     }
     g_scratch[dev] = static_cast<char*>(p);

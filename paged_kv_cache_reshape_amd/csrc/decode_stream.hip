@@ -149,7 +149,6 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
   // Where their pieces lie, worked out now rather than after the stream, when
   // the merge is on the launch's critical path.
   const SeqPieces sp0(s_cum[max(pend0, 0)], s_cum[max(pend0, 0) + 1] - s_cum[max(pend0, 0)], T, R);
-  const SeqPieces sp1(s_cum[max(pend1, 0)], s_cum[max(pend1, 0) + 1] - s_cum[max(pend1, 0)], T, R);
   // The partial state of the range's first sequence, kept in registers until
   // the range is done: a store issued in the middle of the stream would hold
   // up the waits on every load issued after it (one in-order counter covers
@@ -170,9 +169,12 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
       if (gh % ROWS == row) {
         const uint32_t off = (gh * D + col * E) * 4;
 #pragma unroll
-        for (int e = 0; e < E; e += 4)
-          racc.store4(off + 4 * e, acc[gh][e], acc[gh][e + 1], acc[gh][e + 2], acc[gh][e + 3]);
-        if (col == 0) rml.store2(gh * 8, m[gh], l[gh]);
+        for (int e = 0; e < E; e += 4) {
+          const uint32_t wv[4] = {ws_encode(acc[gh][e]), ws_encode(acc[gh][e + 1]),
+                                  ws_encode(acc[gh][e + 2]), ws_encode(acc[gh][e + 3])};
+          racc.store4u(off + 4 * e, wv);
+        }
+        if (col == 0) rml.store2u(gh * 8, ws_encode(m[gh]), ws_encode(l[gh]));
       }
     }
   };
@@ -268,21 +270,12 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
   }
 
   if (pend0 >= 0) publish_state(0, first_m, first_l, first_acc);
-  // Arrivals of the published states; the last worker of a sequence merges
-  // (or the merge kernel that follows, with deferred_merge).
-  if ((pend0 < 0 && pend1 < 0) || a.deferred_merge) return;
-  __builtin_amdgcn_s_waitcnt(0);  // every published store of this wave is complete
-  const int prev0 = pend0 >= 0 ? stream_arrive_issue(a.counters + (size_t)pend0 * Hkv + h, lane) : 0;
-  const int prev1 = pend1 >= 0 ? stream_arrive_issue(a.counters + (size_t)pend1 * Hkv + h, lane) : 0;
-  auto merge_if_last = [&](int b, int prev, const SeqPieces& sp) {
-    if (__builtin_amdgcn_readfirstlane(prev) != sp.count() - 1) return;
-    stream_merge<DT, D, G>(a, b, h, sp, R, lane);
-    if (lane == 0)
-      __hip_atomic_store(a.counters + (size_t)b * Hkv + h, 0, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_SYSTEM);
-  };
-  if (pend0 >= 0) merge_if_last(pend0, prev0, sp0);
-  if (pend1 >= 0) merge_if_last(pend1, prev1, sp1);
+  // A split sequence is merged in this launch by the wave holding its last
+  // piece (or by the merge kernel that follows, with deferred_merge); that
+  // piece is always this wave's first sequence, slot 0.
+  if (pend0 < 0 || r != sp0.r1 || a.deferred_merge) return;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's own published state has landed
+  stream_merge_last<DT, D, G>(a, pend0, h, sp0, R, lane);
 }
 
 // The merges of split sequences as a kernel of their own, launched right

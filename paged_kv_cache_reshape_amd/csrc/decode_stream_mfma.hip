@@ -138,7 +138,6 @@ __global__ __launch_bounds__(stream_mfma_waves(D) * 64) void decode_stream_mfma_
     pend1 = (bl != b0 && jl != nbl - 1) ? bl : -1;
   }
   const SeqPieces sp0(s_cum[max(pend0, 0)], s_cum[max(pend0, 0) + 1] - s_cum[max(pend0, 0)], T, R);
-  const SeqPieces sp1(s_cum[max(pend1, 0)], s_cum[max(pend1, 0) + 1] - s_cum[max(pend1, 0)], T, R);
   // The state of the range's first sequence, kept until the range is done
   // (a store in the middle of the stream would hold up later load waits).
   f32x4 first_o[HT][DT];
@@ -158,10 +157,13 @@ __global__ __launch_bounds__(stream_mfma_waves(D) * 64) void decode_stream_mfma_
         const int gq = 16 * ht + 4 * qj + rr;
         if (gq < G) {
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) racc.store1((gq * D + 16 * dt + qn) * 4, o[ht][dt][rr]);
+          for (int dt = 0; dt < DT; ++dt)
+            __builtin_amdgcn_raw_buffer_store_b32(ws_encode(o[ht][dt][rr]), racc.r,
+                                                  (gq * D + 16 * dt + qn) * 4, 0, kSystemCoherent);
         }
       }
-      if (qj == 0 && 16 * ht + qn < G) rml.store2((16 * ht + qn) * 8, m[ht], l[ht]);
+      if (qj == 0 && 16 * ht + qn < G)
+        rml.store2u((16 * ht + qn) * 8, ws_encode(m[ht]), ws_encode(l[ht]));
     }
   };
 
@@ -260,19 +262,12 @@ __global__ __launch_bounds__(stream_mfma_waves(D) * 64) void decode_stream_mfma_
   }
 
   if (pend0 >= 0) publish_state(0, first_o, first_m, first_l);
-  if ((pend0 < 0 && pend1 < 0) || a.deferred_merge) return;
-  __builtin_amdgcn_s_waitcnt(0);  // every published store of this wave is complete
-  const int prev0 = pend0 >= 0 ? stream_arrive_issue(a.counters + (size_t)pend0 * Hkv + h, lane) : 0;
-  const int prev1 = pend1 >= 0 ? stream_arrive_issue(a.counters + (size_t)pend1 * Hkv + h, lane) : 0;
-  auto merge_if_last = [&](int b, int prev, const SeqPieces& sp) {
-    if (__builtin_amdgcn_readfirstlane(prev) != sp.count() - 1) return;
-    stream_merge<BF16, D, G>(a, b, h, sp, R, lane);
-    if (lane == 0)
-      __hip_atomic_store(a.counters + (size_t)b * Hkv + h, 0, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_SYSTEM);
-  };
-  if (pend0 >= 0) merge_if_last(pend0, prev0, sp0);
-  if (pend1 >= 0) merge_if_last(pend1, prev1, sp1);
+  // A split sequence is merged in this launch by the wave holding its last
+  // piece (or by the merge kernel that follows, with deferred_merge); that
+  // piece is always this wave's first sequence, slot 0.
+  if (pend0 < 0 || r != sp0.r1 || a.deferred_merge) return;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's own published state has landed
+  stream_merge_last<BF16, D, G>(a, pend0, h, sp0, R, lane);
 }
 
 bool stream_mfma_supported(int dtype, int G) { return dtype == PA_DTYPE_BF16 && G == 4; }

@@ -26,6 +26,9 @@ namespace pa {
 constexpr int kStreamMaxSeqs = 2048;
 // Blocks in one worker's range, at most: two table entries per lane.
 constexpr int kStreamMaxRange = 128;
+// Loads of a chunk repeated while a word of an arrived piece is still zero,
+// at most (each is one memory round trip; in practice one or two suffice).
+constexpr int kStreamMergeRetries = 4096;
 
 // Blocks of a sequence of context length c; 0 when empty or longer than the
 // table (those rows are written as zeros or NaN, nothing is streamed).
@@ -153,6 +156,35 @@ __device__ __forceinline__ void stream_range(const DecodeArgs& a, const int* s_c
   }
 }
 
+// Partial states of the balanced schedule are stored encoded, one 32-bit
+// word per float: the bitwise complement of the float, with every NaN first
+// made the one quiet NaN 0x7FC00000.  No float then encodes to 0, so a zero
+// word means "not written yet": a merger that loads a piece's state can
+// tell, word by word, whether the piece's stores have landed (a 4-byte word
+// is read whole), without waiting for the writer to acknowledge them.  The
+// workspace is all zero before a call, and every reader zeroes what it read
+// (each lane what it loaded, after using it), so every call leaves it zero.
+__device__ __forceinline__ float ws_canon(float x) {
+  return x != x ? __uint_as_float(0x7FC00000u) : x;
+}
+__device__ __forceinline__ uint32_t ws_encode(float x) { return ~__float_as_uint(ws_canon(x)); }
+__device__ __forceinline__ float ws_decode(uint32_t w) { return __uint_as_float(~w); }
+
+// Zero a lane's EL consecutive words (EL in {1, 2, 4, 8, 16}) with ordinary
+// stores of exactly that width.
+template <int EL>
+__device__ __forceinline__ void zero_words(uint32_t* p) {
+  if constexpr (EL == 1) {
+    *p = 0u;
+  } else if constexpr (EL == 2) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(0u, 0u);
+  } else {
+    static_assert(EL % 4 == 0, "whole 16-byte pieces");
+#pragma unroll
+    for (int k = 0; k < EL; k += 4) *reinterpret_cast<uint4*>(p + k) = make_uint4(0, 0, 0, 0);
+  }
+}
+
 // Where partial states live: worker r of kv head h keeps up to two, slot 0
 // for the sequence its range starts in, slot 1 for the one it ends in (the
 // sequences between lie wholly inside the range).  Row index of query row
@@ -206,10 +238,11 @@ __device__ __forceinline__ void store_row_part(F32, void* base, size_t i, const 
 }
 
 // Merge of every partial state of (sequence b, kv head h) into the output
-// rows of its G query heads, by one wave.  Pieces are folded in worker
-// order, so the result does not depend on the order in which they were
-// written; up to kBatch pieces are requested in one round trip.  Each lane
-// takes EL consecutive elements of one query row.
+// rows of its G query heads, by one wave of the merge kernel that runs after
+// the stream launch (every piece is stored by then).  Pieces are folded in worker order, so the result does not depend
+// on the order in which they were written; up to kBatch pieces are requested
+// in one round trip.  Each lane takes EL consecutive elements of one query
+// row, and zeroes the words it read once it has used them.
 template <class DT, int D, int G>
 __device__ __forceinline__ void stream_merge(const DecodeArgs& a, int b, int h,
                                              const SeqPieces& sp, int R, int lane) {
@@ -230,11 +263,17 @@ __device__ __forceinline__ void stream_merge(const DecodeArgs& a, int b, int h,
       const size_t row0 = stream_piece_row(h, r, slot, 0, R, G);
       const CoherentRegion racc(a.ws_acc + row0 * D, G * D * 4);
       const CoherentRegion rml(a.ws_ml + row0 * 2, G * 2 * 4);
-      float ml[2];
-      rml.load<2>(gq * 8, ml);
-      pm[u] = ml[0];
-      pl[u] = ml[1];
-      racc.load<EL>((gq * D + d0) * 4, pa[u]);
+      uint32_t ml[2], w[EL];
+      rml.loadu<2>(gq * 8, ml);
+      if constexpr (EL == 1) {
+        w[0] = __builtin_amdgcn_raw_buffer_load_b32(racc.r, (gq * D + d0) * 4, 0, kSystemCoherent);
+      } else {
+        racc.loadu<EL>((gq * D + d0) * 4, w);
+      }
+      pm[u] = ws_decode(ml[0]);
+      pl[u] = ws_decode(ml[1]);
+#pragma unroll
+      for (int k = 0; k < EL; ++k) pa[u][k] = ws_decode(w[k]);
     }
     float Mn = M;
 #pragma unroll
@@ -254,6 +293,20 @@ __device__ __forceinline__ void stream_merge(const DecodeArgs& a, int b, int h,
       }
     }
     M = Mn;
+    // The batch's words are used: zero them (the same lanes, the same
+    // words), with ordinary stores, as stream_merge_last does.
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (p0 + u <= sp.r1) {
+        const int r = p0 + u;
+        const int slot = r == sp.r0 ? sp.slot0 : 0;
+        const size_t row0 = stream_piece_row(h, r, slot, 0, R, G);
+        uint32_t* wacc = reinterpret_cast<uint32_t*>(a.ws_acc + row0 * D) + gq * D + d0;
+        uint32_t* wml = reinterpret_cast<uint32_t*>(a.ws_ml + row0 * 2) + gq * 2;
+        zero_words<2>(wml);
+        zero_words<EL>(wacc);
+      }
+    }
   }
   float x[EL];
 #pragma unroll
@@ -261,15 +314,115 @@ __device__ __forceinline__ void stream_merge(const DecodeArgs& a, int b, int h,
   store_row_part<EL>(DT{}, a.out, ((size_t)b * a.num_q_heads + (size_t)h * G + gq) * D + d0, x);
 }
 
-// Arrival of a worker's piece of (b, h), after its partial state has been
-// published: returns true (in every lane) when this worker is the last of
-// the sequence's `pieces` workers to arrive, and then leaves the counter at
-// zero for the next call.  The caller has waited for its published stores.
-__device__ __forceinline__ int stream_arrive_issue(int32_t* counter, int lane) {
-  int prev = 0;
-  if (lane == 0)
-    prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  return prev;
+
+// In-launch merge of a split (sequence, kv head) by the wave holding its
+// last piece (worker sp.r1), once that wave has stored its own piece: the
+// pieces of workers sp.r0 .. sp.r1 - 1 are waited for by loading their
+// words until none is zero (the encoding has no zero word, so a zero word
+// is a store still on its way).  Those workers belong to this workgroup or
+// to earlier ones (worker index grows with the workgroup index), which the
+// hardware dispatches before this one and which never wait on later ones,
+// so every piece waited for is being computed or done: the same forward-
+// progress argument as a decoupled look-back scan.  The wait is bounded all
+// the same (kStreamMergeRetries round trips), so a broken invariant shows
+// as a wrong row, never as a hang.  There is no arrival counter.
+//
+// Pieces are folded in worker order, kB per round trip, each lane taking EL
+// consecutive elements of one query row; the words are then zeroed with
+// ordinary stores (nothing in this launch reads them again, and the end of
+// the launch writes them back before any later launch reads them).  One
+// rolled loop with a single load site: this code runs once per merge, cold,
+// at the end of the launch, where every extra kilobyte of instructions
+// costs instruction fetches on the critical path.
+template <class DT, int D, int G>
+__device__ __forceinline__ void stream_merge_last(const DecodeArgs& a, int b, int h,
+                                                  const SeqPieces& sp, int R, int lane) {
+  constexpr int EL = G * D / 64;  // elements per lane (1 .. 16)
+  static_assert(EL >= 1 && D % EL == 0, "a lane's elements lie in one row");
+  constexpr int KB = EL <= 4 ? 8 : 4;  // pieces per round trip
+  const int gq = lane * EL / D;
+  const int d0 = lane * EL % D;
+  float M = kNoMax, L = 0.0f, A[EL];
+#pragma unroll
+  for (int k = 0; k < EL; ++k) A[k] = 0.0f;
+  uint32_t wm[KB], wl[KB], wa[KB][EL];
+  int p0 = sp.r0, tries = 0;
+#pragma unroll 1
+  while (p0 <= sp.r1) {
+    // Pieces p0 .. p0 + KB - 1; slots past r1 get a resource of zero bytes
+    // (their loads read nothing and return zeros).
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int r = min(p0 + u, sp.r1);
+      const uint32_t live = p0 + u <= sp.r1 ? 1u : 0u;
+      const size_t row0 = stream_piece_row(h, r, r == sp.r0 ? sp.slot0 : 0, 0, R, G);
+      const CoherentRegion racc(a.ws_acc + row0 * D, live * (G * D * 4));
+      const CoherentRegion rml(a.ws_ml + row0 * 2, live * (G * 2 * 4));
+      uint32_t ml[2];
+      rml.loadu<2>(gq * 8, ml);
+      wm[u] = ml[0];
+      wl[u] = ml[1];
+      if constexpr (EL == 1) {
+        wa[u][0] = __builtin_amdgcn_raw_buffer_load_b32(racc.r, (gq * D + d0) * 4, 0,
+                                                        kSystemCoherent);
+      } else {
+        racc.loadu<EL>((gq * D + d0) * 4, wa[u]);
+      }
+    }
+    bool miss = false;
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      if (p0 + u > sp.r1) continue;
+      miss = miss || wm[u] == 0u || wl[u] == 0u;
+#pragma unroll
+      for (int k = 0; k < EL; ++k) miss = miss || wa[u][k] == 0u;
+    }
+    if (__ballot(miss) != 0 && tries < kStreamMergeRetries) {
+      ++tries;  // a piece is still being computed or stored: load again
+      __builtin_amdgcn_s_sleep(2);
+      continue;
+    }
+    tries = 0;
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+      if (p0 + u <= sp.r1) Mn = fmaxf(Mn, ws_decode(wm[u]));
+    const float f0 = fast_exp2(M - Mn);
+    L *= f0;
+#pragma unroll
+    for (int k = 0; k < EL; ++k) A[k] *= f0;
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      if (p0 + u <= sp.r1) {
+        const float f = fast_exp2(ws_decode(wm[u]) - Mn);
+        L += ws_decode(wl[u]) * f;
+#pragma unroll
+        for (int k = 0; k < EL; ++k) A[k] += ws_decode(wa[u][k]) * f;
+      }
+    }
+    M = Mn;
+    const bool done = p0 + KB > sp.r1;
+    if (done) {
+      float x[EL];
+#pragma unroll
+      for (int k = 0; k < EL; ++k) x[k] = A[k] / L;
+      store_row_part<EL>(DT{}, a.out, ((size_t)b * a.num_q_heads + (size_t)h * G + gq) * D + d0,
+                         x);
+    }
+    // The batch's words are used: zero them (the lanes that read them).
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      if (p0 + u <= sp.r1) {
+        const int r = p0 + u;
+        const size_t row0 = stream_piece_row(h, r, r == sp.r0 ? sp.slot0 : 0, 0, R, G);
+        uint32_t* wacc = reinterpret_cast<uint32_t*>(a.ws_acc + row0 * D) + gq * D + d0;
+        uint32_t* wml = reinterpret_cast<uint32_t*>(a.ws_ml + row0 * 2) + gq * 2;
+        zero_words<2>(wml);
+        zero_words<EL>(wacc);
+      }
+    }
+    p0 += KB;
+  }
 }
 
 }  // namespace pa

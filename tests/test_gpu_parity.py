@@ -603,13 +603,14 @@ def test_one_counter_array_serves_every_geometry(monkeypatch):
                              d["slot_mapping"])
         need = pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads,
                                          w.head_dim, inp["max_blocks"], w.block_size, ps)
-        ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")  # junk
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
         out = pa.paged_attention_decode(d["q"], d["k_cache"], d["v_cache"],
                                         d["block_tables"], d["context_lens"], d["scale"],
                                         partition_size=ps, workspace=ws, counters=cnt)
         ref, _ = oracle_step(inp)
         G.assert_close(G.host_f64(out), ref, w.dtype, f"{name} ps={ps}")
         assert int(cnt.abs().sum()) == 0
+        assert int(ws.count_nonzero()) == 0, "the workspace is left all zero"
 
 
 # ------------------------------------------------------------------ stream schedule
@@ -770,7 +771,7 @@ def test_stream_rerun_bit_identical_and_counters_zero(monkeypatch):
     cnt = torch.zeros(w.num_seqs * w.num_kv_heads, dtype=torch.int32, device="cuda")
     need = pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                      inp["max_blocks"], w.block_size, 0)
-    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     outs = []
     for _ in range(4):
         outs.append(G.host_storage(pa.decode_step(
@@ -778,6 +779,7 @@ def test_stream_rerun_bit_identical_and_counters_zero(monkeypatch):
             d["context_lens"], d["scale"], workspace=ws, counters=cnt)))
         torch.cuda.synchronize()
         assert int(cnt.abs().sum()) == 0
+        assert int(ws.count_nonzero()) == 0, "the workspace is left all zero"
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
 
@@ -859,7 +861,7 @@ def test_graph_replays_match_eager(name, ps, fused, merge, monkeypatch):
     B, hq, hkv = w.num_seqs, w.num_q_heads, w.num_kv_heads
     mb = d["block_tables"].shape[1]
     ps = w.partition_size if ps is None else ps
-    ws = torch.empty(max(pa.decode_workspace_bytes(B, hq, hkv, w.head_dim, mb, w.block_size,
+    ws = torch.zeros(max(pa.decode_workspace_bytes(B, hq, hkv, w.head_dim, mb, w.block_size,
                                                    ps), 256), dtype=torch.uint8, device="cuda")
     cnt = torch.zeros(B * hkv, dtype=torch.int32, device="cuda")
 
