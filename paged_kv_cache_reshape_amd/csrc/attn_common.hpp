@@ -449,21 +449,24 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int npieces, i
     const int e = tid + k * NT;
     if (e < elems) store_out(DT{}, a.out, out_base + e, rA[k] / rL[k]);
   }
-  // Leave the workspace zero, as the balanced schedule's merges expect it:
-  // each thread zeroes the words it loaded, now that it has used them, with
-  // ordinary stores (nothing in this launch reads them again, and the end of
-  // the launch writes them back before any later launch reads them).
-  for (int pc = 0; pc < npieces; ++pc) {
-#pragma unroll
-    for (int k = 0; k < EPT; ++k) a.ws_acc[row_of(pc, qh[k]) * D + dd[k]] = 0.0f;
+  // Leave the workspace zero, as the balanced schedule's merges expect it.
+  // Every piece had landed before it was read (its workgroup waited for its
+  // stores before counting itself in, or it was stored by an earlier
+  // launch), so once every thread has used its loads (the barrier) any
+  // thread may zero any of the rows: 16-byte ordinary stores over whole
+  // rows (nothing in this launch reads them again, and the end of the
+  // launch writes them back before any later launch reads them).
+  __syncthreads();
+  static_assert(D % 4 == 0, "rows of whole 16-byte words");
+  constexpr int Q = D / 4;
+  for (int i = tid; i < npieces * gh * Q; i += NT) {
+    const int ri = i / Q;
+    const size_t r = row_of(ri / gh, ri % gh);
+    reinterpret_cast<uint4*>(a.ws_acc + r * D)[i % Q] = make_uint4(0, 0, 0, 0);
   }
-  for (int c0 = 0; c0 < npieces; c0 += kChunk) {
-    const int n = min(kChunk, npieces - c0);
-    for (int i = tid; i < n * gh; i += NT) {
-      const size_t r = row_of(c0 + i / gh, i % gh);
-      a.ws_ml[r * 2] = 0.0f;
-      a.ws_ml[r * 2 + 1] = 0.0f;
-    }
+  for (int i = tid; i < npieces * gh; i += NT) {
+    const size_t r = row_of(i / gh, i % gh);
+    *reinterpret_cast<uint2*>(a.ws_ml + r * 2) = make_uint2(0, 0);
   }
 }
 
