@@ -559,6 +559,70 @@ def run_prefill(args, torch, pa, cpu_base) -> int:
     return 0
 
 
+TIMELINE_LIB = os.path.join(ROOT, "paged_kv_cache_reshape_amd", "_build_timeline",
+                            "libpagedattn_timeline.so")
+
+
+def timeline_library() -> str:
+    """The measurement build of the library (PA_TIMELINE: the stream kernel's
+    waves stamp the GPU's constant clock), built beside the normal one."""
+    if not os.path.exists(TIMELINE_LIB):
+        from paged_kv_cache_reshape_amd import build as _b
+        _b.build(defines=["PA_TIMELINE=1"], out=TIMELINE_LIB)
+    return TIMELINE_LIB
+
+
+def timeline_summary(lib) -> dict:
+    """Per-wave clock stamps of the latest stream-kernel launch, as offsets
+    from its first wave's start (us): when each wave had requested its first
+    block (prologue), ended its range (stream) and was done (after its merge,
+    if it merged)."""
+    import ctypes
+    words = 16384 * 6
+    buf = (ctypes.c_ulonglong * words)()
+    khz = ctypes.c_int32()
+    lib.pa_debug_timeline.restype = ctypes.c_int32
+    lib.pa_debug_timeline.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    n = lib.pa_debug_timeline(buf, words, ctypes.byref(khz))
+    if n <= 0 or khz.value <= 0:
+        raise RuntimeError("pa_debug_timeline failed")
+    rec = np.frombuffer(buf, dtype=np.uint64).reshape(-1, 6).astype(np.int64)
+    t0 = rec[:, 0]
+    # Every launch of the grid rewrites its waves' records; the latest
+    # launch's waves started within a few microseconds of each other.
+    tick_us = 1000.0 / khz.value
+    last = t0 > t0.max() - int(20.0 / tick_us)
+    r = rec[last]
+    work = (r[:, 3] >= r[:, 0]) & (r[:, 2] >= r[:, 1]) & (r[:, 1] >= r[:, 0])
+    r = r[work]
+    base = r[:, 0].min()
+    us = (r[:, :4] - base) * tick_us
+    merger = r[:, 5] > 0
+    xcc = (r[:, 4] >> 32) & 0xF
+    q = lambda a, p: round(float(np.percentile(a, p)), 2)
+    crit = int(np.argmax(us[:, 3]))
+    return {
+        "kind": "per-wave GPU constant-clock stamps, latest launch of the stream kernel "
+                "(measurement build PA_TIMELINE)",
+        "clock_khz": int(khz.value),
+        "waves": int(len(r)),
+        "mergers": int(merger.sum()),
+        "start_us": {"max": q(us[:, 0], 100)},
+        "prologue_end_us": {"median": q(us[:, 1], 50), "p90": q(us[:, 1], 90),
+                            "max": q(us[:, 1], 100)},
+        "stream_end_us": {"min": q(us[:, 2], 0), "median": q(us[:, 2], 50),
+                          "p90": q(us[:, 2], 90), "max": q(us[:, 2], 100)},
+        "stream_end_us_per_xcd_max": [q(us[xcc == x, 2], 100) for x in range(8)
+                                      if (xcc == x).any()],
+        "merge_us": ({"median": q(us[merger, 3] - us[merger, 2], 50),
+                      "max": q(us[merger, 3] - us[merger, 2], 100)} if merger.any() else None),
+        "done_us_max": q(us[:, 3], 100),
+        "last_wave": {"stream_end_us": round(float(us[crit, 2]), 2),
+                      "done_us": round(float(us[crit, 3]), 2), "merger": bool(merger[crit])},
+        "last_stream_end_to_done_us": round(float(us[:, 3].max() - us[:, 2].max()), 2),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -586,6 +650,9 @@ def main() -> int:
     ap.add_argument("--step-only", action="store_true",
                     help="time the steps only (no separate decode, write or graph timing), "
                          "so that every decode-kernel launch is a fused step: for counter runs")
+    ap.add_argument("--timeline", action="store_true",
+                    help="run the steps on the measurement build of the library (PA_TIMELINE) "
+                         "and add the per-wave timeline of the last launch (balanced schedule)")
     ap.add_argument("--stream-probe", action="store_true",
                     help="print the HBM streaming rates of 8, 64 and 256 reading workgroups "
                          "(read_ceiling.hip rc_stream_probe) as JSON and exit")
@@ -619,6 +686,9 @@ def main() -> int:
     if not os.path.exists(pa.LIB_PATH):
         from paged_kv_cache_reshape_amd import build as _b
         _b.build()
+    if args.timeline:
+        args.step_only = True
+        pa.LIB_PATH = timeline_library()
     pa.load_library()
     if args.workload in synth.PREFILL_WORKLOADS:
         return run_prefill(args, torch, pa, cpu_base)
@@ -762,6 +832,8 @@ def main() -> int:
             "decode_speedup_vs_sdpa": round(sd_ms / (k_mean_s * 1e3), 2),
         }
 
+    timeline = timeline_summary(pa.load_library()) if args.timeline else None
+
     ceilings = None
     if not args.step_only:
         ceilings = read_ceilings(torch, w, inp, kcs, vcs, tables, lens, stream, args.steps)
@@ -824,6 +896,8 @@ def main() -> int:
     }
     if ceilings is not None:
         res["read_ceiling"] = ceilings
+    if timeline is not None:
+        res["timeline"] = timeline
     if prior is not None:
         res["prior_art"] = prior
     if cpu_base is not None:

@@ -20,6 +20,36 @@
 
 namespace pa {
 
+#ifdef PA_TIMELINE
+// Measurement build only (never in the library's default build): every
+// worker wave of the stream kernel records, for the latest launch, the GPU's
+// constant clock at its start, once its first block is requested (end of the
+// prologue), at the end of its range (end of the stream) and when it is done
+// (after its merge, if it merges), with its hardware ids.  Read back with
+// pa_debug_timeline.
+constexpr int kTimelineWaves = 16384;
+constexpr int kTimelineWords = 6;  // t_start, t_prologue, t_stream, t_done, hw_id, flags
+static __device__ unsigned long long pa_timeline[kTimelineWaves * kTimelineWords];
+struct WaveStamps {
+  unsigned long long* rec;
+  __device__ explicit WaveStamps(int global_wave)
+      : rec(global_wave < kTimelineWaves ? pa_timeline + (size_t)global_wave * kTimelineWords
+                                         : nullptr) {}
+  __device__ void put(int k, unsigned long long v) const {
+    if (rec && (threadIdx.x & 63) == 0) rec[k] = v;
+  }
+  __device__ void now(int k) const { put(k, __builtin_amdgcn_s_memrealtime()); }
+};
+#define PA_STAMP(obj, k) (obj).now(k)
+#define PA_STAMP_VALUE(obj, k, v) (obj).put(k, v)
+#else
+struct WaveStamps {
+  __device__ explicit WaveStamps(int) {}
+};
+#define PA_STAMP(obj, k) ((void)0)
+#define PA_STAMP_VALUE(obj, k, v) ((void)0)
+#endif
+
 // 16-byte chunk of E output values: bf16 rounded to nearest even, or f32.
 __device__ __forceinline__ uint4 out_chunk(BF16, const float* x) {
   uint32_t w[4];
@@ -50,6 +80,8 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Hkv = a.num_kv_heads, Hq = a.num_q_heads;
+  const WaveStamps stamps(blockIdx.x * kStreamWaves + wave);
+  PA_STAMP(stamps, 0);
   if constexpr (FUSED) {
     const int hw = stream_heads_per_wg(Hkv);
     if (step_copy_role<DT, D, BS, NT>(a, Hkv / hw * (a.stream_workers / (kStreamWaves / hw))))
@@ -84,6 +116,10 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
   if (r >= R) return;
   StreamRange w;
   stream_range(a, s_cum, T, R, r, lane, w);
+#ifdef PA_TIMELINE
+  PA_STAMP_VALUE(stamps, 4, (unsigned long long)__builtin_amdgcn_s_getreg((31 << 11) | 4) |
+                                ((unsigned long long)__builtin_amdgcn_s_getreg((3 << 11) | 20) << 32));
+#endif
 
   const int row = lane / RL, col = lane % RL;
   const size_t tok_stride = (size_t)Hkv * D;
@@ -132,21 +168,20 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
   Row st;
   int seg_i = 0, seg_j = 0;
   bool poisoned = false;
-  // Sequences whose partial state this worker leaves in slot 0 (the range
-  // starts inside them or they continue past its end) and slot 1 (the last
-  // sequence, when it started inside the range and continues past its end);
-  // -1 for none.  Wave-uniform, known from the range's first and last blocks.
-  int pend0, pend1;
+  // The sequence whose partial state this worker leaves in slot 0 (its range
+  // starts inside it, or it continues past the range's end); -1 for none.
+  // Wave-uniform, known from the range's first block.  (The range's last
+  // sequence, when it starts inside the range and continues past its end,
+  // leaves slot 1, published as soon as it is reached.)
+  int pend0;
   {
-    const int v0 = w.seqblk(0), vl = w.seqblk(w.n - 1);
+    const int v0 = w.seqblk(0);
     const int b0 = (v0 >> 16) & 0x7FFF, j0 = v0 & 0xFFFF;
-    const int bl = (vl >> 16) & 0x7FFF, jl = vl & 0xFFFF;
-    const int nb0 = (w.ctx(0) + BS - 1) / BS, nbl = (w.ctx(w.n - 1) + BS - 1) / BS;
+    const int nb0 = (w.ctx(0) + BS - 1) / BS;
     const bool first_whole = j0 == 0 && nb0 - j0 <= w.n;
     pend0 = first_whole ? -1 : b0;
-    pend1 = (bl != b0 && jl != nbl - 1) ? bl : -1;
   }
-  // Where their pieces lie, worked out now rather than after the stream, when
+  // Where its pieces lie, worked out now rather than after the stream, when
   // the merge is on the launch's critical path.
   const SeqPieces sp0(s_cum[max(pend0, 0)], s_cum[max(pend0, 0) + 1] - s_cum[max(pend0, 0)], T, R);
   // The partial state of the range's first sequence, kept in registers until
@@ -259,6 +294,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
     fetch(clampi(p), p < w.n, sl[p]);
     __builtin_amdgcn_sched_barrier(0);
   }
+  PA_STAMP(stamps, 1);
   for (int i0 = 0; i0 < w.n; i0 += PF) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
@@ -269,13 +305,20 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
     }
   }
 
+  PA_STAMP(stamps, 2);
   if (pend0 >= 0) publish_state(0, first_m, first_l, first_acc);
   // A split sequence is merged in this launch by the wave holding its last
   // piece (or by the merge kernel that follows, with deferred_merge); that
   // piece is always this wave's first sequence, slot 0.
-  if (pend0 < 0 || r != sp0.r1 || a.deferred_merge) return;
+  if (pend0 < 0 || r != sp0.r1 || a.deferred_merge) {
+    PA_STAMP(stamps, 3);
+    PA_STAMP_VALUE(stamps, 5, 0ull);
+    return;
+  }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's own published state has landed
   stream_merge_last<DT, D, G>(a, pend0, h, sp0, R, lane);
+  PA_STAMP(stamps, 3);
+  PA_STAMP_VALUE(stamps, 5, 1ull + (unsigned long long)(sp0.r1 - sp0.r0));
 }
 
 // The merges of split sequences as a kernel of their own, launched right
@@ -358,3 +401,25 @@ hipError_t launch_stream(int dtype, int D, int BS, int G, const DecodeArgs& a, h
 }
 
 }  // namespace pa
+
+#ifdef PA_TIMELINE
+// Copy the stream kernel's per-wave records of the latest launch on the
+// current device to host memory (entries of 6 words, as laid out above;
+// records of waves a launch did not have keep older values), and report the
+// constant clock's frequency in kHz.  Measurement build only.
+extern "C" int32_t pa_debug_timeline(unsigned long long* host, int64_t max_words,
+                                     int32_t* clock_khz) {
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(pa::pa_timeline)) != hipSuccess) return -1;
+  const int64_t words = (int64_t)pa::kTimelineWaves * pa::kTimelineWords;
+  const int64_t n = max_words < words ? max_words : words;
+  if (hipDeviceSynchronize() != hipSuccess) return -1;
+  if (hipMemcpy(host, p, (size_t)n * 8, hipMemcpyDeviceToHost) != hipSuccess) return -1;
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    return -1;
+  *clock_khz = khz;
+  return (int32_t)n;
+}
+#endif

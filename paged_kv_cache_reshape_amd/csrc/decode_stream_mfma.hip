@@ -125,17 +125,15 @@ __global__ __launch_bounds__(stream_mfma_waves(D) * 64) void decode_stream_mfma_
   Tile st;
   int seg_i = 0, seg_j = 0;
   bool poisoned = false;
-  // Sequences whose partial state this worker leaves in slot 0 and slot 1,
-  // as in the vector-ALU worker; -1 for none.
-  int pend0, pend1;
+  // The sequence whose partial state this worker leaves in slot 0, as in the
+  // vector-ALU worker; -1 for none.
+  int pend0;
   {
-    const int v0 = w.seqblk(0), vl = w.seqblk(w.n - 1);
+    const int v0 = w.seqblk(0);
     const int b0 = (v0 >> 16) & 0x7FFF, j0 = v0 & 0xFFFF;
-    const int bl = (vl >> 16) & 0x7FFF, jl = vl & 0xFFFF;
-    const int nb0 = (w.ctx(0) + BS - 1) / BS, nbl = (w.ctx(w.n - 1) + BS - 1) / BS;
+    const int nb0 = (w.ctx(0) + BS - 1) / BS;
     const bool first_whole = j0 == 0 && nb0 - j0 <= w.n;
     pend0 = first_whole ? -1 : b0;
-    pend1 = (bl != b0 && jl != nbl - 1) ? bl : -1;
   }
   const SeqPieces sp0(s_cum[max(pend0, 0)], s_cum[max(pend0, 0) + 1] - s_cum[max(pend0, 0)], T, R);
   // The state of the range's first sequence, kept until the range is done

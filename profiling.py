@@ -11,6 +11,8 @@ Commands (run on the CSV files a GPU run wrote):
   python profiling.py counters OUT_MD --kernel NAME \\
       --command "<...>" COUNTER_CSV [COUNTER_CSV ...]
 
+  python profiling.py timeline BENCH_TIMELINE_JSON OUT_MD --command "<...>"
+
 ``traffic`` scales the per-dispatch FETCH_SIZE and WRITE_SIZE of the decode
 kernel by what the same counters read for the plain copy kernels in the same
 run (PyTorch cloning one K cache, a copy of known size), and records the hash
@@ -179,6 +181,35 @@ def counters_summary(csvs: list, kernel: str, out_md: str, command: str) -> dict
     return avg
 
 
+def timeline_md(bench_json: str, out_md: str, command: str) -> None:
+    """The per-wave timeline that ``bench.py --timeline`` printed, as a short
+    markdown summary."""
+    res = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    t = res["timeline"]
+    lines = [f"# Per-wave timeline of the stream kernel, {res['config']['workload'].split(':')[0]}",
+             "", "Command:", "", "```", command, "```", "",
+             f"Step time in the same run (measurement build): {res['us_per_step']} us; "
+             f"{t['waves']} worker waves, {t['mergers']} of them merge a split sequence; "
+             f"constant clock {t['clock_khz']} kHz. Offsets from the first wave's start (us):",
+             "", "| event | median | p90 | max |", "|---|---|---|---|",
+             f"| wave start | | | {t['start_us']['max']} |",
+             f"| first block requested (prologue end) | {t['prologue_end_us']['median']} | "
+             f"{t['prologue_end_us']['p90']} | {t['prologue_end_us']['max']} |",
+             f"| range streamed (stream end) | {t['stream_end_us']['median']} | "
+             f"{t['stream_end_us']['p90']} | {t['stream_end_us']['max']} |",
+             f"| done | | | {t['done_us_max']} |", "",
+             f"Earliest stream end: {t['stream_end_us']['min']} us. Latest stream end per XCD: "
+             f"{', '.join(str(x) for x in t['stream_end_us_per_xcd_max'])} us."]
+    if t.get("merge_us"):
+        lines.append(f"Merge (stream end to done, merging waves): median {t['merge_us']['median']}"
+                     f" us, max {t['merge_us']['max']} us.")
+    lw = t["last_wave"]
+    lines.append(f"The last wave to finish ended its stream at {lw['stream_end_us']} us and was "
+                 f"done at {lw['done_us']} us ({'a merger' if lw['merger'] else 'not a merger'}); "
+                 f"the last stream end to the last wave done: {t['last_stream_end_to_done_us']} us.")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -194,6 +225,10 @@ def main(argv=None) -> int:
     f.add_argument("--command", required=True)
     f.add_argument("--fused-step", action="store_true",
                    help="the counters come from `bench.py --step-only` (fused-step launches)")
+    tl = sub.add_parser("timeline")
+    tl.add_argument("bench_json")
+    tl.add_argument("out_md")
+    tl.add_argument("--command", required=True)
     c = sub.add_parser("counters")
     c.add_argument("out_md")
     c.add_argument("csvs", nargs="+")
@@ -202,6 +237,8 @@ def main(argv=None) -> int:
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         trace_summary(a.stats_csv, a.out_md, a.command)
+    elif a.cmd == "timeline":
+        timeline_md(a.bench_json, a.out_md, a.command)
     elif a.cmd == "counters":
         print(json.dumps(counters_summary(a.csvs, a.kernel, a.out_md, a.command), indent=1))
     else:
