@@ -572,8 +572,9 @@ def timeline_library() -> str:
     return TIMELINE_LIB
 
 
-def timeline_summary(lib) -> dict:
-    """Per-wave clock stamps of the latest stream-kernel launch, as offsets
+def timeline_summary(lib, reader: str = "pa_debug_timeline") -> dict:
+    """Per-wave clock stamps of the last stream-kernel launch since the last
+    read (the reader clears the records), as offsets
     from its first wave's start (us): when each wave had requested its first
     block (prologue), ended its range (stream) and was done (after its merge,
     if it merged)."""
@@ -581,26 +582,38 @@ def timeline_summary(lib) -> dict:
     words = 16384 * 6
     buf = (ctypes.c_ulonglong * words)()
     khz = ctypes.c_int32()
-    lib.pa_debug_timeline.restype = ctypes.c_int32
-    lib.pa_debug_timeline.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
-    n = lib.pa_debug_timeline(buf, words, ctypes.byref(khz))
+    fn = getattr(lib, reader)
+    fn.restype = ctypes.c_int32
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    n = fn(buf, words, ctypes.byref(khz))
     if n <= 0 or khz.value <= 0:
         raise RuntimeError("pa_debug_timeline failed")
     rec = np.frombuffer(buf, dtype=np.uint64).reshape(-1, 6).astype(np.int64)
-    t0 = rec[:, 0]
-    # Every launch of the grid rewrites its waves' records; the latest
-    # launch's waves started within a few microseconds of each other.
     tick_us = 1000.0 / khz.value
-    last = t0 > t0.max() - int(20.0 / tick_us)
-    r = rec[last]
-    work = (r[:, 3] >= r[:, 0]) & (r[:, 2] >= r[:, 1]) & (r[:, 1] >= r[:, 0])
-    r = r[work]
+    # The reader clears the records, and every launch of the same grid
+    # rewrites its waves' records: only the last launch's waves hold stamps,
+    # and those that stream (not the copy workgroups) hold all four.
+    r = rec[(rec[:, 0] > 0) & (rec[:, 1] >= rec[:, 0]) & (rec[:, 2] >= rec[:, 1])
+            & (rec[:, 3] >= rec[:, 2])]
+    if len(r) == 0:
+        raise RuntimeError("no stream-kernel wave recorded a timeline")
     base = r[:, 0].min()
     us = (r[:, :4] - base) * tick_us
     merger = r[:, 5] > 0
     xcc = (r[:, 4] >> 32) & 0xF
     q = lambda a, p: round(float(np.percentile(a, p)), 2)
     crit = int(np.argmax(us[:, 3]))
+    # Compute unit of each wave: XCC, shader engine, shader array and CU of
+    # HW_ID; waves per CU tell whether some CUs host more workgroups.
+    hw = r[:, 4]
+    cu_key = (((hw >> 32) & 0xF) << 8) | (((hw >> 13) & 0x7) << 5) | (((hw >> 12) & 1) << 4) \
+        | ((hw >> 8) & 0xF)
+    _, per_cu = np.unique(cu_key, return_counts=True)
+    waves_per_cu = {int(k): int(v) for k, v in zip(*np.unique(per_cu, return_counts=True))}
+    cu_of = {int(k): i for i, k in enumerate(np.unique(cu_key))}
+    cu_end = np.zeros(len(cu_of))
+    for k, e in zip(cu_key, us[:, 2]):
+        cu_end[cu_of[int(k)]] = max(cu_end[cu_of[int(k)]], e)
     return {
         "kind": "per-wave GPU constant-clock stamps, latest launch of the stream kernel "
                 "(measurement build PA_TIMELINE)",
@@ -620,6 +633,9 @@ def timeline_summary(lib) -> dict:
         "last_wave": {"stream_end_us": round(float(us[crit, 2]), 2),
                       "done_us": round(float(us[crit, 3]), 2), "merger": bool(merger[crit])},
         "last_stream_end_to_done_us": round(float(us[:, 3].max() - us[:, 2].max()), 2),
+        "compute_units": len(cu_of),
+        "cus_by_waves_hosted": waves_per_cu,
+        "cu_stream_end_us": {"min": q(cu_end, 0), "median": q(cu_end, 50), "max": q(cu_end, 100)},
     }
 
 
@@ -832,7 +848,18 @@ def main() -> int:
             "decode_speedup_vs_sdpa": round(sd_ms / (k_mean_s * 1e3), 2),
         }
 
-    timeline = timeline_summary(pa.load_library()) if args.timeline else None
+    timeline = None
+    if args.timeline:
+        if part != 0:
+            raise SystemExit("--timeline covers the balanced schedule's kernels only")
+        reader = ("pa_debug_timeline_mfma" if decode_kernel_name(w, part)
+                  == "decode_stream_mfma_kernel" else "pa_debug_timeline")
+        timeline_summary(pa.load_library(), reader)  # clears the records
+        # Back-to-back steps as in the timed region; each launch rewrites its
+        # waves' records, so the read holds the last one.
+        for i in range(args.steps):
+            step(args.warmup + args.steps + i)
+        timeline = timeline_summary(pa.load_library(), reader)
 
     ceilings = None
     if not args.step_only:

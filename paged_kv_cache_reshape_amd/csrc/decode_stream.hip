@@ -15,40 +15,11 @@
 // reads the stored copy, so the result is the write followed by the read,
 // bit for bit.
 #include "stream_sched.hpp"
+#include "timeline.hpp"
 
 #include "decode_launch.hpp"
 
 namespace pa {
-
-#ifdef PA_TIMELINE
-// Measurement build only (never in the library's default build): every
-// worker wave of the stream kernel records, for the latest launch, the GPU's
-// constant clock at its start, once its first block is requested (end of the
-// prologue), at the end of its range (end of the stream) and when it is done
-// (after its merge, if it merges), with its hardware ids.  Read back with
-// pa_debug_timeline.
-constexpr int kTimelineWaves = 16384;
-constexpr int kTimelineWords = 6;  // t_start, t_prologue, t_stream, t_done, hw_id, flags
-static __device__ unsigned long long pa_timeline[kTimelineWaves * kTimelineWords];
-struct WaveStamps {
-  unsigned long long* rec;
-  __device__ explicit WaveStamps(int global_wave)
-      : rec(global_wave < kTimelineWaves ? pa_timeline + (size_t)global_wave * kTimelineWords
-                                         : nullptr) {}
-  __device__ void put(int k, unsigned long long v) const {
-    if (rec && (threadIdx.x & 63) == 0) rec[k] = v;
-  }
-  __device__ void now(int k) const { put(k, __builtin_amdgcn_s_memrealtime()); }
-};
-#define PA_STAMP(obj, k) (obj).now(k)
-#define PA_STAMP_VALUE(obj, k, v) (obj).put(k, v)
-#else
-struct WaveStamps {
-  __device__ explicit WaveStamps(int) {}
-};
-#define PA_STAMP(obj, k) ((void)0)
-#define PA_STAMP_VALUE(obj, k, v) ((void)0)
-#endif
 
 // 16-byte chunk of E output values: bf16 rounded to nearest even, or f32.
 __device__ __forceinline__ uint4 out_chunk(BF16, const float* x) {
@@ -116,10 +87,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
   if (r >= R) return;
   StreamRange w;
   stream_range(a, s_cum, T, R, r, lane, w);
-#ifdef PA_TIMELINE
-  PA_STAMP_VALUE(stamps, 4, (unsigned long long)__builtin_amdgcn_s_getreg((31 << 11) | 4) |
-                                ((unsigned long long)__builtin_amdgcn_s_getreg((3 << 11) | 20) << 32));
-#endif
+  PA_STAMP_IDS(stamps);
 
   const int row = lane / RL, col = lane % RL;
   const size_t tok_stride = (size_t)Hkv * D;
@@ -402,24 +370,5 @@ hipError_t launch_stream(int dtype, int D, int BS, int G, const DecodeArgs& a, h
 
 }  // namespace pa
 
-#ifdef PA_TIMELINE
-// Copy the stream kernel's per-wave records of the latest launch on the
-// current device to host memory (entries of 6 words, as laid out above;
-// records of waves a launch did not have keep older values), and report the
-// constant clock's frequency in kHz.  Measurement build only.
-extern "C" int32_t pa_debug_timeline(unsigned long long* host, int64_t max_words,
-                                     int32_t* clock_khz) {
-  void* p = nullptr;
-  if (hipGetSymbolAddress(&p, HIP_SYMBOL(pa::pa_timeline)) != hipSuccess) return -1;
-  const int64_t words = (int64_t)pa::kTimelineWaves * pa::kTimelineWords;
-  const int64_t n = max_words < words ? max_words : words;
-  if (hipDeviceSynchronize() != hipSuccess) return -1;
-  if (hipMemcpy(host, p, (size_t)n * 8, hipMemcpyDeviceToHost) != hipSuccess) return -1;
-  int dev = 0, khz = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
-    return -1;
-  *clock_khz = khz;
-  return (int32_t)n;
-}
-#endif
+
+PA_TIMELINE_READER(pa_debug_timeline)

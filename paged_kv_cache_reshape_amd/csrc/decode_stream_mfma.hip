@@ -21,6 +21,7 @@
 // the launch reads the stored copy.
 #include "mfma_attn.hpp"
 #include "stream_sched.hpp"
+#include "timeline.hpp"
 
 #include "decode_launch.hpp"
 
@@ -45,6 +46,8 @@ __global__ __launch_bounds__(stream_mfma_waves(D) * 64) void decode_stream_mfma_
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Hkv = a.num_kv_heads, Hq = a.num_q_heads;
+  const WaveStamps stamps(blockIdx.x * NW + wave);
+  PA_STAMP(stamps, 0);
   const int HW = stream_heads_per_wg(Hkv);
   const int RW = NW / HW;
   const int ngr = Hkv / HW;
@@ -66,6 +69,7 @@ __global__ __launch_bounds__(stream_mfma_waves(D) * 64) void decode_stream_mfma_
   if (r >= R) return;
   StreamRange w;
   stream_range(a, s_cum, T, R, r, lane, w);
+  PA_STAMP_IDS(stamps);
 
   const int row = lane / RL, col = lane % RL;
   const int qn = lane & 15, qj = lane >> 4;  // MFMA lane coordinates
@@ -249,6 +253,7 @@ __global__ __launch_bounds__(stream_mfma_waves(D) * 64) void decode_stream_mfma_
     fetch(clampi(p), p < w.n, sl[p]);
     __builtin_amdgcn_sched_barrier(0);
   }
+  PA_STAMP(stamps, 1);
   for (int i0 = 0; i0 < w.n; i0 += PF) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
@@ -259,13 +264,20 @@ __global__ __launch_bounds__(stream_mfma_waves(D) * 64) void decode_stream_mfma_
     }
   }
 
+  PA_STAMP(stamps, 2);
   if (pend0 >= 0) publish_state(0, first_o, first_m, first_l);
   // A split sequence is merged in this launch by the wave holding its last
   // piece (or by the merge kernel that follows, with deferred_merge); that
   // piece is always this wave's first sequence, slot 0.
-  if (pend0 < 0 || r != sp0.r1 || a.deferred_merge) return;
+  if (pend0 < 0 || r != sp0.r1 || a.deferred_merge) {
+    PA_STAMP(stamps, 3);
+    PA_STAMP_VALUE(stamps, 5, 0ull);
+    return;
+  }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's own published state has landed
   stream_merge_last<BF16, D, G>(a, pend0, h, sp0, R, lane);
+  PA_STAMP(stamps, 3);
+  PA_STAMP_VALUE(stamps, 5, 1ull + (unsigned long long)(sp0.r1 - sp0.r0));
 }
 
 bool stream_mfma_supported(int dtype, int G) { return dtype == PA_DTYPE_BF16 && G == 4; }
@@ -292,3 +304,5 @@ hipError_t launch_stream_mfma(int D, int BS, int G, const DecodeArgs& a, hipStre
 }
 
 }  // namespace pa
+
+PA_TIMELINE_READER(pa_debug_timeline_mfma)

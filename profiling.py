@@ -203,6 +203,11 @@ def timeline_md(bench_json: str, out_md: str, command: str) -> None:
     if t.get("merge_us"):
         lines.append(f"Merge (stream end to done, merging waves): median {t['merge_us']['median']}"
                      f" us, max {t['merge_us']['max']} us.")
+    if t.get("compute_units"):
+        hosted = ", ".join(f"{n} CUs with {k} waves" for k, n in t["cus_by_waves_hosted"].items())
+        ce = t["cu_stream_end_us"]
+        lines.append(f"Compute units used: {t['compute_units']} ({hosted}). Latest stream end per "
+                     f"CU: min {ce['min']}, median {ce['median']}, max {ce['max']} us.")
     lw = t["last_wave"]
     lines.append(f"The last wave to finish ended its stream at {lw['stream_end_us']} us and was "
                  f"done at {lw['done_us']} us ({'a merger' if lw['merger'] else 'not a merger'}); "
