@@ -56,7 +56,7 @@ DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_reshape_amd", "csrc", f)
                for f in ("decode_partition.hip", "decode_mfma.hip", "decode_stream.hip",
                          "decode_stream_mfma.hip",
                          "attn_common.hpp", "mfma_attn.hpp", "stream_sched.hpp", "common.hpp",
-                         "decode_launch.hpp", "decode_api.hip", "options.hpp")]
+                         "decode_launch.hpp", "decode_api.hip", "options.hpp", "timeline.hpp")]
 # Worker processes the CPU baseline spreads the oracle over: the host's cores,
 # at most 16 (one GPU's share of a shared host).
 CPU_POOL_MAX = 16
@@ -588,8 +588,14 @@ def timeline_summary(lib, reader: str = "pa_debug_timeline") -> dict:
     n = fn(buf, words, ctypes.byref(khz))
     if n <= 0 or khz.value <= 0:
         raise RuntimeError("pa_debug_timeline failed")
-    rec = np.frombuffer(buf, dtype=np.uint64).reshape(-1, 6).astype(np.int64)
-    tick_us = 1000.0 / khz.value
+    return timeline_stats(np.frombuffer(buf, dtype=np.uint64).reshape(-1, 6).astype(np.int64),
+                          khz.value)
+
+
+def timeline_stats(rec: np.ndarray, clock_khz: int) -> dict:
+    """Summary of per-wave records [t_start, t_prologue, t_stream, t_done,
+    hw ids, pieces merged (0: not a merger)], clock ticks at clock_khz."""
+    tick_us = 1000.0 / clock_khz
     # The reader clears the records, and every launch of the same grid
     # rewrites its waves' records: only the last launch's waves hold stamps,
     # and those that stream (not the copy workgroups) hold all four.
@@ -617,7 +623,7 @@ def timeline_summary(lib, reader: str = "pa_debug_timeline") -> dict:
     return {
         "kind": "per-wave GPU constant-clock stamps, latest launch of the stream kernel "
                 "(measurement build PA_TIMELINE)",
-        "clock_khz": int(khz.value),
+        "clock_khz": int(clock_khz),
         "waves": int(len(r)),
         "mergers": int(merger.sum()),
         "start_us": {"max": q(us[:, 0], 100)},

@@ -121,3 +121,37 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120, cwd=root)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_timeline_stats_and_summary(tmp_path):
+    """The per-wave timeline summary on hand-made records: four streaming
+    waves on two compute units (100 MHz clock, so one tick is 0.01 us), one
+    of them a merger, and a copy wave that only stamped its start."""
+    def hw(xcc, se, cu):
+        return (xcc << 32) | (se << 13) | (cu << 8)
+    base = 1_000_000
+    rec = np.zeros((8, 6), dtype=np.int64)
+    #            start        prologue      stream end     done           ids         merged
+    rec[0] = [base,        base + 280,   base + 2400,   base + 2410,   hw(0, 1, 3), 0]
+    rec[1] = [base + 10,   base + 300,   base + 2500,   base + 2800,   hw(0, 1, 3), 3]
+    rec[2] = [base + 5,    base + 260,   base + 2100,   base + 2105,   hw(1, 0, 7), 0]
+    rec[3] = [base + 20,   base + 290,   base + 2600,   base + 2605,   hw(1, 0, 7), 0]
+    rec[4] = [base + 30,   0,            0,             0,             hw(1, 0, 2), 0]
+    t = bench.timeline_stats(rec, 100_000)
+    assert t["waves"] == 4 and t["mergers"] == 1
+    assert t["prologue_end_us"]["max"] == 3.0
+    assert t["stream_end_us"]["min"] == 21.0 and t["stream_end_us"]["max"] == 26.0
+    assert t["done_us_max"] == 28.0
+    assert t["merge_us"]["median"] == 3.0
+    assert t["last_wave"] == {"stream_end_us": 25.0, "done_us": 28.0, "merger": True}
+    assert t["last_stream_end_to_done_us"] == 2.0
+    assert t["compute_units"] == 2 and t["cus_by_waves_hosted"] == {2: 2}
+    assert t["cu_stream_end_us"]["min"] == 25.0 and t["cu_stream_end_us"]["max"] == 26.0
+    j = tmp_path / "tl.json"
+    j.write_text(json.dumps({"us_per_step": 31.8, "timeline": t,
+                             "config": {"workload": "qwen3_0p6b: B=32"}}) + "\n")
+    md = tmp_path / "tl.md"
+    profiling.timeline_md(str(j), str(md), "python bench.py --timeline")
+    text = md.read_text()
+    assert "| range streamed (stream end) |" in text and "2 CUs with 2 waves" in text
+
