@@ -116,9 +116,10 @@ __device__ __forceinline__ float collect(const float* p) {
 }
 
 // The same system-coherent policy (sc0 sc1, what a system-scope atomic
-// store or load carries on gfx950) for whole 16- or 8-byte pieces, through a
-// buffer resource over a wave-uniform base: partial states move in a few
-// wide accesses instead of one 4-byte transaction per value.
+// store or load carries on gfx950) for whole 16- or 8-byte pieces of 32-bit
+// words (the balanced schedule's encoded partial states), through a buffer
+// resource over a wave-uniform base: partial states move in a few wide
+// accesses instead of one 4-byte transaction per value.
 constexpr int kBufferWord3 = 0x00020000;  // gfx9 raw buffer, 32-bit data format
 constexpr int kSystemCoherent = 17;       // cache-policy operand: sc0 | sc1
 constexpr int kLoadNT = 2;                // cache-policy operand of data read once: nt
@@ -128,19 +129,6 @@ struct CoherentRegion {
   // `bytes` (an access past it reads 0 and writes nothing).
   __device__ __forceinline__ CoherentRegion(float* base, uint32_t bytes)
       : r(__builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, kBufferWord3)) {}
-  __device__ __forceinline__ void store4(uint32_t off, float a, float b, float c, float d) const {
-    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-    const u4 v = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kSystemCoherent);
-  }
-  __device__ __forceinline__ void store2(uint32_t off, float a, float b) const {
-    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-    const u2 v = {__float_as_uint(a), __float_as_uint(b)};
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kSystemCoherent);
-  }
-  __device__ __forceinline__ void store1(uint32_t off, float a) const {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), r, off, 0, kSystemCoherent);
-  }
   // Raw 32-bit words (encoded partial states of the balanced schedule).
   __device__ __forceinline__ void store4u(uint32_t off, const uint32_t* w) const {
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
@@ -166,24 +154,6 @@ struct CoherentRegion {
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * k, 0, kSystemCoherent);
 #pragma unroll
         for (int t = 0; t < 4; ++t) w[4 * k + t] = v[t];
-      }
-    }
-  }
-  // N consecutive floats (N in {1, 2, 4, 8, 16}) at byte offset off.
-  template <int N>
-  __device__ __forceinline__ void load(uint32_t off, float* x) const {
-    if constexpr (N == 1) {
-      x[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSystemCoherent));
-    } else if constexpr (N == 2) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kSystemCoherent);
-      x[0] = __uint_as_float(v[0]);
-      x[1] = __uint_as_float(v[1]);
-    } else {
-#pragma unroll
-      for (int k = 0; k < N / 4; ++k) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * k, 0, kSystemCoherent);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) x[4 * k + t] = __uint_as_float(v[t]);
       }
     }
   }
