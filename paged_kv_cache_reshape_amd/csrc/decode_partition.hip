@@ -54,9 +54,11 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
 
   st.reset();
   // A block's rows through buffer loads over that block: 16 bytes a lane at
-  // d = E col of token t ROWS + row.  The prefetch past a wave's last block
-  // (live false) gets a resource of zero bytes, so it reads nothing instead
-  // of the last block once more.
+  // d = E col of token t ROWS + row.  The resource covers the block's rows
+  // below the context length only, so the rows past it in a sequence's last
+  // block read nothing (they return zeros, and are masked anyway); the
+  // prefetch past a wave's last block (live false) gets a resource of zero
+  // bytes, so it reads nothing instead of the last block once more.
   constexpr int ROWS = Sh::ROWS;
   const uint32_t tok_bytes = (uint32_t)((size_t)Hkv * D * sizeof(S));
   const uint32_t blk_bytes = tok_bytes * BS;
@@ -65,7 +67,8 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
   const char* vbase = static_cast<const char*>(a.v_cache);
   auto fetch = [&](int j, bool live, uint4 (&kr)[NI], uint4 (&vr)[NI]) {
     const size_t off = (size_t)w.block(j) * blk_bytes;
-    const uint32_t n = live ? blk_bytes : 0u;
+    const int rows = min(BS, ctx - (blk0 + j) * BS);  // >= 1 for a live block
+    const uint32_t n = live ? (uint32_t)rows * tok_bytes : 0u;
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + off), 0, n, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rv =

@@ -105,14 +105,17 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
     uint4 k[NI], v[NI], q[G], nk, nv;
   };
   // Block i's rows through buffer loads over that block (16 bytes a lane at
-  // d = E col of token t ROWS + row).  A prefetch past the range's end
+  // d = E col of token t ROWS + row).  The resource covers the rows below the
+  // sequence's length only: rows past it in the last block read nothing (they
+  // return zeros, and are masked anyway).  A prefetch past the range's end
   // (live false) gets a resource of zero bytes: its loads return zeros and
   // read nothing, where re-reading the last block would cost a block of HBM
   // traffic per wave.
   auto fetch = [&](int i, bool live, Slot& sl) {
     const size_t off = (size_t)w.entry(i) * blk_stride * sizeof(S);
     const int b = (w.seqblk(i) >> 16) & 0x7FFF;
-    const uint32_t n = live ? blk_bytes : 0u;
+    const int rows = min(BS, w.ctx(i) - (w.seqblk(i) & 0xFFFF) * BS);  // >= 1
+    const uint32_t n = live ? (uint32_t)rows * tok_bytes : 0u;
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + off), 0, n, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rv =
