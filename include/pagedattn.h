@@ -16,7 +16,9 @@
  *   - LLAISYS README, implemented-features list: C++ backend behind a C API
  *     called from Python; online softmax with a running max and running sum;
  *     grouped heads by broadcasting; a multi-block reduction finished by the
- *     last block to arrive (fence + atomic counter) instead of a second launch.
+ *     last block to arrive (fence + atomic counter) instead of a second launch
+ *     (the fixed-partition schedule does so; the balanced schedule finishes
+ *     in the launch too, by the worker holding a sequence's last block).
  *   - MinivLLM article, "What the Two Benchmark Scripts Compare": paged
  *     decode attention as its own kernel, blockwise online softmax.
  *

@@ -84,8 +84,9 @@ bool deferred_merge(int max_parts) {
 }
 
 // Where the stream schedule merges split sequences: in the launch, by the
-// last worker to finish (default), or in a merge kernel launched after it
-// (PAGEDATTN_MERGE=separate; PAGEDATTN_MERGE=inkernel forces the default).
+// worker holding each one's last block (default), or in a merge kernel
+// launched after it (PAGEDATTN_MERGE=separate; PAGEDATTN_MERGE=inkernel
+// forces the default).
 bool stream_deferred_merge() { return options().merge == 1; }
 
 // Worker waves in all that the stream schedule aims for.  With 1 or 2 query

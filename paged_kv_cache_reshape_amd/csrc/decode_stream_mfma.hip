@@ -4,12 +4,13 @@
 // The schedule is that of decode_stream.hip -- each kv head's block list cut
 // into equal ranges, one wave per range, up to four neighbouring kv heads
 // per workgroup over one or more consecutive ranges (eight waves at head_dim
-// 64, four at 128), split sequences merged by the last piece to arrive -- and the
-// fold of a block is that of the matrix-core decode (mfma_attn.hpp): the
-// wave stages the block's K and V rows of its kv head in its own LDS tile
-// and runs q.k and p.v as 16x16x32 MFMAs over its G query rows.  With four
-// query heads per kv head the vector-ALU worker's multiply-adds and
-// reductions per byte, which grow with G, set its pace rather than HBM.
+// 64, four at 128), split sequences merged by the worker holding their last
+// block (stream_merge_last) -- and the fold of a block is that of the
+// matrix-core decode (mfma_attn.hpp): the wave stages the block's K and V
+// rows of its kv head in its own LDS tile and runs q.k and p.v as 16x16x32
+// MFMAs over its G query rows.  With four query heads per kv head the
+// vector-ALU worker's multiply-adds and reductions per byte, which grow
+// with G, set its pace rather than HBM.
 //
 // Rows of a block at or past the sequence's length are zeroed in registers
 // before staging (the rows exist -- the block is in the pool -- but may hold

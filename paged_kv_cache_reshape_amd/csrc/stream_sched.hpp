@@ -3,9 +3,10 @@
 // into R equal ranges of consecutive blocks, one per worker wave.  A worker
 // streams its range, finishing a sequence's state whenever the sequence ends
 // inside it; a sequence whose blocks fall in several ranges leaves one
-// partial state per range, and the last of those workers to finish merges
-// them (log-sum-exp merge, the last-block pattern of the LLAISYS README,
-// CUDA argmax item).
+// partial state per range, and the worker holding its last block merges
+// them in the same launch (log-sum-exp merge; a multi-block reduction
+// finished inside the launch, as in the LLAISYS README, CUDA argmax item,
+// with the finishing block chosen statically: see stream_merge_last).
 //
 // Why: with fixed partitions per sequence the busiest compute unit streams a
 // whole 1024-token partition while others idle; equal ranges give every
