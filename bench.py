@@ -579,7 +579,7 @@ def timeline_summary(lib, reader: str = "pa_debug_timeline") -> dict:
     block (prologue), ended its range (stream) and was done (after its merge,
     if it merged)."""
     import ctypes
-    words = 16384 * 6
+    words = 16384 * 8
     buf = (ctypes.c_ulonglong * words)()
     khz = ctypes.c_int32()
     fn = getattr(lib, reader)
@@ -588,13 +588,14 @@ def timeline_summary(lib, reader: str = "pa_debug_timeline") -> dict:
     n = fn(buf, words, ctypes.byref(khz))
     if n <= 0 or khz.value <= 0:
         raise RuntimeError("pa_debug_timeline failed")
-    return timeline_stats(np.frombuffer(buf, dtype=np.uint64).reshape(-1, 6).astype(np.int64),
+    return timeline_stats(np.frombuffer(buf, dtype=np.uint64).reshape(-1, 8).astype(np.int64),
                           khz.value)
 
 
 def timeline_stats(rec: np.ndarray, clock_khz: int) -> dict:
     """Summary of per-wave records [t_start, t_prologue, t_stream, t_done,
-    hw ids, pieces merged (0: not a merger)], clock ticks at clock_khz."""
+    hw ids, pieces merged (0: not a merger), t_lengths, t_range], clock ticks
+    at clock_khz (t_lengths / t_range: 0 where not recorded)."""
     tick_us = 1000.0 / clock_khz
     # The reader clears the records, and every launch of the same grid
     # rewrites its waves' records: only the last launch's waves hold stamps,
@@ -627,6 +628,12 @@ def timeline_stats(rec: np.ndarray, clock_khz: int) -> dict:
         "waves": int(len(r)),
         "mergers": int(merger.sum()),
         "start_us": {"max": q(us[:, 0], 100)},
+        "lengths_end_us": ({"median": q((r[:, 6] - base) * tick_us, 50),
+                            "max": q((r[:, 6] - base) * tick_us, 100)}
+                           if r.shape[1] > 6 and (r[:, 6] > 0).all() else None),
+        "range_end_us": ({"median": q((r[:, 7] - base) * tick_us, 50),
+                          "max": q((r[:, 7] - base) * tick_us, 100)}
+                         if r.shape[1] > 7 and (r[:, 7] > 0).all() else None),
         "prologue_end_us": {"median": q(us[:, 1], 50), "p90": q(us[:, 1], 90),
                             "max": q(us[:, 1], 100)},
         "stream_end_us": {"min": q(us[:, 2], 0), "median": q(us[:, 2], 50),

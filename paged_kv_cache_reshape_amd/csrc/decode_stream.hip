@@ -72,13 +72,23 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
 
   // Empty sequences give zero rows, lengths past the table NaN rows; each is
   // written for this workgroup's kv heads by one workgroup of the group.
-  const int T = stream_prefix<NT>(a, BS, s_cum, s_part, [&](int b, int c) {
+  auto empty_rows = [&](int b, int c) {
     if (b % wgs_per_group != kwg) return;
     const size_t base = ((size_t)b * Hq + (size_t)gg * HW * G) * D;
     const float fill = c == 0 ? 0.0f : __builtin_nanf("");
     for (int e = 0; e < HW * G * D; ++e) store_out(DT{}, a.out, base + e, fill);
-  });
+  };
+  // Up to 64 sequences: the set-up in each wave's registers; else through LDS.
+  const bool small = a.num_seqs <= kStreamSmallSeqs;
+  int sm_start = 0, sm_len = 0;
+  const int T = small ? stream_prefix_small(a, BS, lane, wave == 0, sm_start, sm_len, empty_rows)
+                      : stream_prefix<NT>(a, BS, s_cum, s_part, empty_rows);
+  // First block of sequence b in the kv head's list (b <= B, wave-uniform).
+  auto seq_start = [&](int b) {
+    return small ? small_seq_start(sm_start, b, a.num_seqs, T) : s_cum[b];
+  };
 
+  PA_STAMP(stamps, 6);
   // With fewer blocks than workers, the first T workers take one block each
   // and the rest none: every worker in [0, R) then holds a block, which the
   // piece count of a merge relies on.
@@ -86,7 +96,11 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
   const int r = kwg * RW + wave / HW;
   if (r >= R) return;
   StreamRange w;
-  stream_range(a, s_cum, T, R, r, lane, w);
+  if (small)
+    stream_range_small(a, sm_start, sm_len, T, R, r, lane, w);
+  else
+    stream_range(a, s_cum, T, R, r, lane, w);
+  PA_STAMP(stamps, 7);
   PA_STAMP_IDS(stamps);
 
   const int row = lane / RL, col = lane % RL;
@@ -154,7 +168,8 @@ __global__ __launch_bounds__(kStreamWaves * 64) void decode_stream_kernel(Decode
   }
   // Where its pieces lie, worked out now rather than after the stream, when
   // the merge is on the launch's critical path.
-  const SeqPieces sp0(s_cum[max(pend0, 0)], s_cum[max(pend0, 0) + 1] - s_cum[max(pend0, 0)], T, R);
+  const int p0b = max(pend0, 0);
+  const SeqPieces sp0(seq_start(p0b), seq_start(p0b + 1) - seq_start(p0b), T, R);
   // The partial state of the range's first sequence, kept in registers until
   // the range is done: a store issued in the middle of the stream would hold
   // up the waits on every load issued after it (one in-order counter covers

@@ -59,17 +59,29 @@ __global__ __launch_bounds__(stream_mfma_waves(D) * 64) void decode_stream_mfma_
   const int h = gg * HW + wave % HW;
   const int wgs_per_group = a.stream_workers / RW;
 
-  const int T = stream_prefix<NT>(a, BS, s_cum, s_part, [&](int b, int c) {
+  auto empty_rows = [&](int b, int c) {
     if (b % wgs_per_group != kwg) return;
     const size_t base = ((size_t)b * Hq + (size_t)gg * HW * G) * D;
     const float fill = c == 0 ? 0.0f : __builtin_nanf("");
     for (int e = 0; e < HW * G * D; ++e) store_out(BF16{}, a.out, base + e, fill);
-  });
+  };
+  // Up to 64 sequences: the set-up in each wave's registers; else through LDS.
+  const bool small = a.num_seqs <= kStreamSmallSeqs;
+  int sm_start = 0, sm_len = 0;
+  const int T = small ? stream_prefix_small(a, BS, lane, wave == 0, sm_start, sm_len, empty_rows)
+                      : stream_prefix<NT>(a, BS, s_cum, s_part, empty_rows);
+  // First block of sequence b in the kv head's list (b <= B, wave-uniform).
+  auto seq_start = [&](int b) {
+    return small ? small_seq_start(sm_start, b, a.num_seqs, T) : s_cum[b];
+  };
   const int R = min(a.stream_workers, T);
   const int r = kwg * RW + wave / HW;
   if (r >= R) return;
   StreamRange w;
-  stream_range(a, s_cum, T, R, r, lane, w);
+  if (small)
+    stream_range_small(a, sm_start, sm_len, T, R, r, lane, w);
+  else
+    stream_range(a, s_cum, T, R, r, lane, w);
   PA_STAMP_IDS(stamps);
 
   const int row = lane / RL, col = lane % RL;
@@ -140,7 +152,8 @@ __global__ __launch_bounds__(stream_mfma_waves(D) * 64) void decode_stream_mfma_
     const bool first_whole = j0 == 0 && nb0 - j0 <= w.n;
     pend0 = first_whole ? -1 : b0;
   }
-  const SeqPieces sp0(s_cum[max(pend0, 0)], s_cum[max(pend0, 0) + 1] - s_cum[max(pend0, 0)], T, R);
+  const int p0b = max(pend0, 0);
+  const SeqPieces sp0(seq_start(p0b), seq_start(p0b + 1) - seq_start(p0b), T, R);
   // The state of the range's first sequence, kept until the range is done
   // (a store in the middle of the stream would hold up later load waits).
   f32x4 first_o[HT][DT];

@@ -157,6 +157,85 @@ __device__ __forceinline__ void stream_range(const DecodeArgs& a, const int* s_c
   }
 }
 
+// The same set-up for batches of at most 64 sequences, held in registers:
+// every wave reads the lengths (lane b: sequence b) and scans them itself,
+// so there is no LDS and no workgroup barrier, and a range's sequences are
+// found with one ballot and lane shuffles instead of dependent LDS reads.
+// Measured on MI355X (Qwen3-shaped batch, per-wave clock stamps): the LDS
+// set-up took 0.56 us between the prefix sum and the first table request.
+constexpr int kStreamSmallSeqs = 64;
+
+// Lane b < B gets the first block of sequence b in `start` (the exclusive
+// prefix sum of blocks) and its length in `len`; returns T.  `empty(b, c)`
+// is called for sequences that take no blocks, by the first wave only.
+template <class Empty>
+__device__ __forceinline__ int stream_prefix_small(const DecodeArgs& a, int bs, int lane,
+                                                   bool first_wave, int& start, int& len,
+                                                   Empty&& empty) {
+  const int B = a.num_seqs;
+  len = lane < B ? a.context_lens[lane] : 0;
+  const int nb = lane < B ? seq_blocks(len, bs, a.max_blocks) : 0;
+  if (first_wave && lane < B && nb == 0) empty(lane, len);
+  int x = nb;  // inclusive scan over the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(x, o, 64);
+    if (lane >= o) x += t;
+  }
+  start = x - nb;
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+// First block of sequence b (b <= B, wave-uniform) from those registers.
+__device__ __forceinline__ int small_seq_start(int start, int b, int B, int T) {
+  return b < B ? __builtin_amdgcn_readlane(start, b) : T;
+}
+
+// stream_range from those registers (B <= 64).
+__device__ __forceinline__ void stream_range_small(const DecodeArgs& a, int start, int len, int T,
+                                                   int R, int r, int lane, StreamRange& w) {
+  const int B = a.num_seqs;
+  w.s = range_start(r, T, R);
+  w.n = range_start(r + 1, T, R) - w.s;
+  w.ent[0] = w.ent[1] = 0;
+  w.bj[0] = w.bj[1] = 0;
+  w.cx[0] = w.cx[1] = 0;
+  const int s = w.s, e = w.s + w.n;
+  // Sequence of block s: the last b with start(b) <= s (empty sequences share
+  // the next one's start, so the last such b holds the block).
+  const int b0 = __popcll(__ballot(lane < B && start <= s)) - 1;
+  // Starts of the sequences after b0 that fall inside the range (T past the
+  // last sequence, which is >= e, so fewer than 64 of them).
+  const int idx = b0 + 1 + lane;
+  const int nxt = __shfl(start, min(idx, 63), 64);
+  const int cs = idx < B ? nxt : T;
+  const int nk = __popcll(__ballot(cs < e));
+  const int g0 = s + lane, g1 = s + 64 + lane;
+  int b_0 = b0, b_1 = b0;
+  for (int k = 0; k < nk; ++k) {
+    const int c = __builtin_amdgcn_readlane(cs, k);
+    b_0 += c <= g0;
+    b_1 += c <= g1;
+  }
+  // Start and length of each lane's two sequences, shuffled with every lane
+  // active (b_0, b_1 < B).
+  const int st[2] = {__shfl(start, b_0, 64), __shfl(start, b_1, 64)};
+  const int ln[2] = {__shfl(len, b_0, 64), __shfl(len, b_1, 64)};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = 64 * h + lane;
+    if (i < w.n) {
+      const int b = h ? b_1 : b_0;
+      const int j = (h ? g1 : g0) - st[h];
+      const int id = a.block_tables[(size_t)b * a.max_blocks + j];
+      const bool bad = id < 0 || id >= a.num_blocks;
+      w.ent[h] = bad ? 0 : id;
+      w.bj[h] = (b << 16) | j | (bad ? (int)0x80000000u : 0);
+      w.cx[h] = ln[h];
+    }
+  }
+}
+
 // Partial states of the balanced schedule are stored encoded, one 32-bit
 // word per float: the bitwise complement of the float, with every NaN first
 // made the one quiet NaN 0x7FC00000.  No float then encodes to 0, so a zero

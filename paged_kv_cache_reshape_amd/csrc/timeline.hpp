@@ -17,7 +17,9 @@ namespace pa {
 
 #ifdef PA_TIMELINE
 constexpr int kTimelineWaves = 16384;
-constexpr int kTimelineWords = 6;  // t_start, t_prologue, t_stream, t_done, hw ids, pieces merged
+// t_start, t_prologue, t_stream, t_done, hw ids, pieces merged, t_lengths (prefix
+// sum of the lengths done), t_range (range's table entries requested)
+constexpr int kTimelineWords = 8;
 static __device__ unsigned long long pa_timeline[kTimelineWaves * kTimelineWords];
 struct WaveStamps {
   unsigned long long* rec;

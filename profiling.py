@@ -193,6 +193,10 @@ def timeline_md(bench_json: str, out_md: str, command: str) -> None:
              f"constant clock {t['clock_khz']} kHz. Offsets from the first wave's start (us):",
              "", "| event | median | p90 | max |", "|---|---|---|---|",
              f"| wave start | | | {t['start_us']['max']} |",
+             *([f"| lengths read and prefix-summed | {t['lengths_end_us']['median']} | | "
+                f"{t['lengths_end_us']['max']} |"] if t.get("lengths_end_us") else []),
+             *([f"| range's table entries requested | {t['range_end_us']['median']} | | "
+                f"{t['range_end_us']['max']} |"] if t.get("range_end_us") else []),
              f"| first block requested (prologue end) | {t['prologue_end_us']['median']} | "
              f"{t['prologue_end_us']['p90']} | {t['prologue_end_us']['max']} |",
              f"| range streamed (stream end) | {t['stream_end_us']['median']} | "
