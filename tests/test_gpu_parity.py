@@ -698,6 +698,26 @@ def test_stream_many_short_sequences(monkeypatch):
     check_stream(inp, "stream many short")
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(8, 4, 128), (16, 4, 64)])
+@pytest.mark.parametrize("B", [63, 64, 65])
+def test_stream_set_up_either_side_of_64_sequences(B, hq, hkv, d, monkeypatch):
+    """Up to 64 sequences the balanced schedule sets ranges up in each wave's
+    registers, above that through LDS: both workers (G = 2 vector ALU, G = 4
+    matrix cores) against the oracle, with empty
+    sequences first, last and in between (ranges of a few blocks, so every
+    range's start falls in a different place)."""
+    G.setopt(monkeypatch, "PAGEDATTN_SCHEDULE", "stream")
+    G.setopt(monkeypatch, "PAGEDATTN_STREAM_WORKERS", 512)
+    rng = np.random.default_rng(1064 + B)
+    ctx = rng.integers(1, 700, size=B).astype(np.int32)
+    ctx[[0, B // 3, B - 1]] = 0
+    w = synth.Workload(f"stream_b{B}_g{hq // hkv}", B, hq, hkv, d, 16, "bf16",
+                       ("uniform", 1, 700), seed=64 + B)
+    inp = synth.make_inputs(w, context_lens=ctx)
+    say("stream set-up", B, "sequences, G", hq // hkv, "D", d)
+    check_stream(inp, f"stream B={B} G={hq // hkv} D={d}")
+
+
 @pytest.mark.parametrize("name", ["qwen3_0p6b", "llama32_1b"])
 def test_stream_library_choice(name):
     """The library's own choice for the Qwen3- and Llama-3.2-shaped batches is
