@@ -407,7 +407,7 @@ __device__ __forceinline__ void stream_merge(const DecodeArgs& a, int b, int h,
 // the same (kStreamMergeRetries round trips), so a broken invariant shows
 // as a wrong row, never as a hang.  There is no arrival counter.
 //
-// Pieces are folded in worker order, kB per round trip, each lane taking EL
+// Pieces are folded in worker order, KB per round trip, each lane taking EL
 // consecutive elements of one query row; the words are then zeroed with
 // ordinary stores (nothing in this launch reads them again, and the end of
 // the launch writes them back before any later launch reads them).  One
