@@ -586,6 +586,38 @@ def test_side_stream_and_given_out():
     assert np.array_equal(G.host_storage(out), base)
 
 
+def test_one_workspace_serves_both_schedules():
+    """One workspace and one counter array shared by calls that lay partial
+    states out differently: the balanced schedule (vector-ALU and matrix-core
+    workers, whose merges take a zero word for "not stored yet") alternating
+    with fixed partitions (merged in the launch, or by the merge kernel at 16
+    or more partitions).  Every call must leave the workspace all zero, or a
+    later balanced call would read a stale state as stored."""
+    cases = [("qwen3_0p6b", 0), ("qwen3_0p6b", 64), ("llama32_1b", 0), ("qwen3_0p6b", 256),
+             ("bf16_d128_bs16_g16", 32), ("qwen3_0p6b", 0), ("llama32_1b", 0),
+             ("llama32_1b", 128)]
+    need = 256
+    for name, ps in cases:
+        w = inputs_for(name)["workload"]
+        need = max(need, pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                                                   w.head_dim, inputs_for(name)["max_blocks"],
+                                                   w.block_size, ps))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    cnt = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    for name, ps in cases:
+        inp = inputs_for(name)
+        w = inp["workload"]
+        say("shared workspace", name, "partition", ps or "library choice")
+        d = G.upload(inp)
+        out = pa.decode_step(d["q"], d["key"], d["value"], d["k_cache"], d["v_cache"],
+                             d["block_tables"], d["context_lens"], d["scale"],
+                             partition_size=ps, workspace=ws, counters=cnt)
+        ref, _ = oracle_step(inp)
+        G.assert_close(G.host_f64(out), ref, w.dtype, f"{name} ps={ps}")
+        assert int(cnt.abs().sum()) == 0
+        assert int(ws.count_nonzero()) == 0, f"{name} ps={ps}: the workspace is left all zero"
+
+
 def test_one_counter_array_serves_every_geometry(monkeypatch):
     """Counters left at zero by each call: alternate two geometries whose
     partial results overlap differently, with one shared counter array
